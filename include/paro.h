@@ -1,0 +1,167 @@
+/*
+ * paro.h -- C ABI of the MI355X (gfx950) rotated W4A16 linear library (libparo.so).
+ *
+ * The operation is the runtime hot path of ParoQuant ("ParoQuant: pairwise
+ * rotations that survive deployment", hungho77.github.io, and the arXiv
+ * abstract of "ParoQuant: Pairwise Rotation Quantization for Efficient
+ * Reasoning LLM Inference"):
+ *
+ *   - K stages of Givens rotations over disjoint channel pairs; for a pair
+ *     (i, j) with angle t:  x'_i = cos t * x_i + sin t * x_j,
+ *                           x'_j = -sin t * x_i + cos t * x_j
+ *     (section "A rotation small enough to execute", the 2x2 equation);
+ *     every channel is in exactly one pair of each stage, so the pairs of a
+ *     stage are independent;
+ *   - channel-wise scaling after the rotations; at runtime the activations are
+ *     divided by s, at build time the weights are rotated by the same stages
+ *     and multiplied by s ("weight transformations are folded and quantized",
+ *     same section), so that transform(x) . W'^T = x . W^T;
+ *   - a group-wise asymmetric INT4 weight-only linear (W4A16, group 128 along
+ *     the input dimension; section "My reduced-calibration experiment"), one
+ *     per layer right after the transform (section "From fake quantization to
+ *     a real TensorRT engine").
+ *
+ * Conventions shared by every call
+ *   - Shapes: x is [M][D] row-major float16, W is [N][D] row-major float16,
+ *     y = transform(x) . dequant(W')^T is [M][N] row-major.
+ *   - Packed weights: qweight uint8 [N][D/2] (byte t of row n holds channel 2t
+ *     in bits 0..3 and channel 2t+1 in bits 4..7); scales float16 [N][D/128];
+ *     zeros float16 [N][D/128] holding integers 0..15. Dequantized weight:
+ *     (q - z) * scale.
+ *   - Quantizer (per row n, group g of 128 channels of the folded weights b,
+ *     in float64): scale = fp16_rne(max((max b - min b) / 15, 1e-5));
+ *     z = clip(rint(-min b / scale), 0, 15); q = clip(rint(b / scale) + z, 0, 15).
+ *   - Every pointer argument named *_dev, x, y, W, qweight, scales, zeros, ws
+ *     is a DEVICE pointer on the current HIP device; *_host arguments are host
+ *     pointers. Device pointers must be 16-byte aligned.
+ *   - The caller owns every buffer. The library allocates nothing, frees
+ *     nothing and keeps no mutable global state; calls are re-entrant.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     is asynchronous, except paro_rotation_prepare, which synchronizes
+ *     `stream` once its upload is enqueued.
+ *   - Errors: argument and shape checks run on the host before anything is
+ *     enqueued and return a status; a failed launch returns PARO_EHIP. Faults
+ *     inside a kernel surface at the caller's next synchronization.
+ *   - Limits: D even, D % 128 == 0, 128 <= D <= PARO_MAX_D; 0 <= K <=
+ *     PARO_MAX_K; M >= 0 and N >= 0 (zero sizes enqueue nothing and succeed).
+ */
+#ifndef PARO_H
+#define PARO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARO_GROUP 128
+#define PARO_MAX_D 16384
+#define PARO_MAX_K 64
+
+typedef enum {
+  PARO_OK = 0,
+  PARO_EINVAL = 1,     /* null or misaligned pointer, negative size, bad dtype, aliasing */
+  PARO_ESHAPE = 2,     /* D odd, D % 128 != 0, D outside [128, PARO_MAX_D], K outside [0, PARO_MAX_K] */
+  PARO_EPAIRS = 3,     /* a stage does not pair every channel exactly once */
+  PARO_ESCALE = 4,     /* a channel scale is not finite and > 0, or an angle is not finite */
+  PARO_EWORKSPACE = 5, /* workspace missing or smaller than paro_workspace_bytes() */
+  PARO_EHIP = 6        /* the HIP runtime reported an error (launch or copy) */
+} paro_status;
+
+typedef enum { PARO_F16 = 0, PARO_F32 = 1 } paro_dtype; /* element type of y */
+
+/* A prepared transform: plain data, copyable. `dev` points at the caller-owned
+ * device descriptor written by paro_rotation_prepare. */
+typedef struct {
+  int32_t K;
+  int32_t D;
+  void* dev;
+} paro_rotation;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* paro_status_str(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int paro_version(void);
+
+/* Bytes of device memory a descriptor for (K, D) needs; 0 if (K, D) is invalid. */
+size_t paro_rotation_bytes(int K, int D);
+
+/*
+ * paro_rotation_prepare -- validate a transform and upload its descriptor.
+ *
+ * Defines the transform of section "A rotation small enough to execute":
+ *   pairs_host  int32 [K][D/2][2]: stage k's pairs (i, j); each stage must use
+ *               every channel 0..D-1 exactly once (else PARO_EPAIRS);
+ *   theta_host  float32 [K][D/2]: one angle per pair per stage (finite);
+ *   scale_host  float32 [D]: channel scales s > 0 (finite).
+ * cos/sin are evaluated in float64 by the C library and rounded once to
+ * float32; 1/s is rounded once to float32. The descriptor (stage pairs as two
+ * uint16, (cos, sin) as float32, 1/s and s as float32) is copied into
+ * desc_dev (desc_bytes >= paro_rotation_bytes(K, D)) on `stream`, which is then
+ * synchronized so the host arrays may be released on return. On success *out
+ * = {K, D, desc_dev}. Nothing is written to the device on an error.
+ */
+paro_status paro_rotation_prepare(int K, int D, const int32_t* pairs_host, const float* theta_host,
+                                  const float* scale_host, void* desc_dev, size_t desc_bytes,
+                                  paro_rotation* out, void* stream);
+
+/*
+ * paro_pack_weights -- build-time weight fold and INT4 quantization.
+ *
+ * For each row of W (float16 [N][D]), in float64 with no fused multiply-add:
+ * apply the K stages (stage 1 first, same expressions as the activation side),
+ * multiply by s, then quantize each 128-channel group as stated at the top and
+ * pack the codes. Writes qweight [N][D/2], scales [N][D/128], zeros [N][D/128].
+ * The outputs are bit-identical to the stated float64 definition
+ * ("weight transformations are folded and quantized", section "A rotation
+ * small enough to execute"; "real INT4 packing", section "From fake
+ * quantization to a real TensorRT engine"). W must not alias the outputs.
+ */
+paro_status paro_pack_weights(const paro_rotation* r, int N, const void* W, uint8_t* qweight,
+                              void* scales, void* zeros, void* stream);
+
+/*
+ * paro_rotate -- runtime activation-side transform (section "A rotation small
+ * enough to execute": the inverse activation-side transformation runs right
+ * before the INT4 linear). xout[m][:] = fp16(G_K...G_1 x[m][:] / s), computed
+ * in float32 and rounded once to float16. x and xout are float16 [M][D] and
+ * must not overlap.
+ */
+paro_status paro_rotate(const paro_rotation* r, int M, const void* x, void* xout, void* stream);
+
+/* Workspace bytes paro_w4a16_linear / paro_rotated_linear need for (M, D, N);
+ * may be 0. A larger workspace is always accepted. */
+size_t paro_workspace_bytes(int M, int D, int N);
+
+/*
+ * paro_w4a16_linear -- plain group-wise INT4 weight-only linear (section "From
+ * fake quantization to a real TensorRT engine": one group-wise INT4 GEMM per
+ * layer): y[m][n] = sum_g scale[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g]),
+ * products of float16 values exact, accumulation in float32, y stored as
+ * ydtype (PARO_F16 rounds once). x float16 [M][D]; y [M][N] must not overlap
+ * any input. ws is a device buffer of ws_bytes >= paro_workspace_bytes(M, D, N)
+ * (may be NULL when that is 0).
+ */
+paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t* qweight,
+                              const void* scales, const void* zeros, void* y, int ydtype, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * paro_rotated_linear -- the fused runtime path: the activation transform of
+ * paro_rotate (float32, rounded once to float16 as the linear's 16-bit
+ * operand) immediately followed by the INT4 linear of paro_w4a16_linear, with
+ * the weights packed by paro_pack_weights for the same transform. Small M runs
+ * as one kernel; large M as a transform kernel writing into ws followed by the
+ * MFMA GEMM, on `stream`. Arguments as in paro_w4a16_linear, with D = r->D.
+ */
+paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void* x,
+                                const uint8_t* qweight, const void* scales, const void* zeros,
+                                void* y, int ydtype, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARO_H */

@@ -1,0 +1,260 @@
+"""Python binding of libparo (the MI355X rotated W4A16 linear library).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. PyTorch provides device memory and the current stream. The names
+mirror the C ABI in include/paro.h.
+
+Importing this package loads ``libparo.so`` from the package directory; if it
+is missing the import fails loudly (build it with ``python -m
+rotated_linear_amd._build``). There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libparo.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rotated_linear_amd._build`")
+
+# PyTorch-ROCm ships its own HIP runtime (soname libamdhip64.so.7). Importing torch first makes
+# libparo's libamdhip64.so.7 dependency bind to that already-loaded runtime, so device pointers
+# and streams handed over from torch belong to the runtime that launches the kernels.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped() -> set:
+    try:
+        with open("/proc/self/maps") as f:
+            return {ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln}
+    except OSError:
+        return set()
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError(f"two HIP runtimes are loaded in this process: {sorted(_hip_runtimes_mapped())}")
+
+GROUP = 128
+MAX_D = 16384
+MAX_K = 64
+F16, F32 = 0, 1
+
+STATUS = {0: "PARO_OK", 1: "PARO_EINVAL", 2: "PARO_ESHAPE", 3: "PARO_EPAIRS", 4: "PARO_ESCALE",
+          5: "PARO_EWORKSPACE", 6: "PARO_EHIP"}
+
+
+class paro_rotation(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("D", ctypes.c_int32), ("dev", ctypes.c_void_p)]
+
+
+_vp, _sz, _i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_lib.paro_status_str.restype = ctypes.c_char_p
+_lib.paro_status_str.argtypes = [_i]
+_lib.paro_version.restype = _i
+_lib.paro_rotation_bytes.restype = _sz
+_lib.paro_rotation_bytes.argtypes = [_i, _i]
+_lib.paro_rotation_prepare.restype = _i
+_lib.paro_rotation_prepare.argtypes = [_i, _i, _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(paro_rotation), _vp]
+_lib.paro_pack_weights.restype = _i
+_lib.paro_pack_weights.argtypes = [ctypes.POINTER(paro_rotation), _i, _vp, _vp, _vp, _vp, _vp]
+_lib.paro_rotate.restype = _i
+_lib.paro_rotate.argtypes = [ctypes.POINTER(paro_rotation), _i, _vp, _vp, _vp]
+_lib.paro_workspace_bytes.restype = _sz
+_lib.paro_workspace_bytes.argtypes = [_i, _i, _i]
+_lib.paro_w4a16_linear.restype = _i
+_lib.paro_w4a16_linear.argtypes = [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+_lib.paro_rotated_linear.restype = _i
+_lib.paro_rotated_linear.argtypes = [ctypes.POINTER(paro_rotation), _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp,
+                                     _sz, _vp]
+
+EXPORTS = ("paro_status_str", "paro_version", "paro_rotation_bytes", "paro_rotation_prepare",
+           "paro_pack_weights", "paro_rotate", "paro_workspace_bytes", "paro_w4a16_linear",
+           "paro_rotated_linear")
+
+
+class ParoError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {_lib.paro_status_str(status).decode()}")
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise ParoError(status, call)
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def paro_status_str(status: int) -> str:
+    return _lib.paro_status_str(status).decode()
+
+
+def paro_version() -> int:
+    return _lib.paro_version()
+
+
+def paro_rotation_bytes(K: int, D: int) -> int:
+    return _lib.paro_rotation_bytes(K, D)
+
+
+def paro_workspace_bytes(M: int, D: int, N: int) -> int:
+    return _lib.paro_workspace_bytes(M, D, N)
+
+
+# --------------------------------------------------------------------------- #
+# torch plumbing
+# --------------------------------------------------------------------------- #
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _want(t, dtype, shape, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Rotation:
+    """A prepared transform: the device descriptor (a uint8 tensor) and its C handle."""
+
+    def __init__(self, K: int, D: int, desc, handle: paro_rotation):
+        self.K, self.D, self.desc, self.handle = K, D, desc, handle
+
+    @property
+    def ptr(self):
+        return ctypes.byref(self.handle)
+
+
+def paro_rotation_prepare(pairs, theta, scale, device="cuda") -> Rotation:
+    """pairs int32 [K][D/2][2], theta float32 [K][D/2], scale float32 [D] (host arrays)."""
+    torch = _torch()
+    pairs = np.ascontiguousarray(np.asarray(pairs, np.int32))
+    theta = np.ascontiguousarray(np.asarray(theta, np.float32))
+    scale = np.ascontiguousarray(np.asarray(scale, np.float32))
+    D = int(scale.shape[0])
+    K = int(pairs.shape[0]) if pairs.ndim == 3 else 0
+    if pairs.ndim != 3 or pairs.shape[1:] != (D // 2, 2) or theta.shape != (K, D // 2):
+        raise ValueError("pairs must be [K][D/2][2] and theta [K][D/2] with D = len(scale)")
+    nbytes = _lib.paro_rotation_bytes(K, D)
+    if nbytes == 0:
+        raise ParoError(2, "paro_rotation_bytes")
+    desc = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    handle = paro_rotation()
+    with torch.cuda.device(desc.device):
+        st = _lib.paro_rotation_prepare(K, D, pairs.ctypes.data_as(_vp), theta.ctypes.data_as(_vp),
+                                        scale.ctypes.data_as(_vp), _ptr(desc), nbytes, ctypes.byref(handle),
+                                        _stream_ptr(desc.device))
+    _check(st, "paro_rotation_prepare")
+    return Rotation(K, D, desc, handle)
+
+
+def paro_pack_weights(rot: Rotation, W, out=None):
+    """W float16 [N][D] on the GPU -> (qweight uint8 [N][D/2], scales f16 [N][D/128], zeros f16 [N][D/128])."""
+    torch = _torch()
+    N, D = int(W.shape[0]), rot.D
+    _want(W, torch.float16, (N, D), "W")
+    if out is None:
+        qw = torch.empty((N, D // 2), dtype=torch.uint8, device=W.device)
+        sc = torch.empty((N, D // GROUP), dtype=torch.float16, device=W.device)
+        z = torch.empty((N, D // GROUP), dtype=torch.float16, device=W.device)
+    else:
+        qw, sc, z = out
+    with torch.cuda.device(W.device):
+        _check(_lib.paro_pack_weights(rot.ptr, N, _ptr(W), _ptr(qw), _ptr(sc), _ptr(z), _stream_ptr(W.device)),
+               "paro_pack_weights")
+    return qw, sc, z
+
+
+def paro_rotate(rot: Rotation, x, out=None):
+    """x float16 [M][D] -> transformed activations float16 [M][D]."""
+    torch = _torch()
+    M = int(x.shape[0])
+    _want(x, torch.float16, (M, rot.D), "x")
+    xo = torch.empty_like(x) if out is None else out
+    with torch.cuda.device(x.device):
+        _check(_lib.paro_rotate(rot.ptr, M, _ptr(x), _ptr(xo), _stream_ptr(x.device)), "paro_rotate")
+    return xo
+
+
+def _linear_out(M, N, out_dtype, device, out):
+    torch = _torch()
+    if out is not None:
+        return out
+    return torch.empty((M, N), dtype=out_dtype, device=device)
+
+
+def _ydt(t):
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("y must be float16 or float32")
+
+
+def paro_w4a16_linear(x, qweight, scales, zeros, out_dtype=None, out=None, ws=None):
+    """Plain group-wise INT4 linear: y = x . dequant(qweight, scales, zeros)^T."""
+    torch = _torch()
+    M, D = int(x.shape[0]), int(x.shape[1])
+    N = int(qweight.shape[0])
+    _want(x, torch.float16, (M, D), "x")
+    _want(qweight, torch.uint8, (N, D // 2), "qweight")
+    _want(scales, torch.float16, (N, D // GROUP), "scales")
+    _want(zeros, torch.float16, (N, D // GROUP), "zeros")
+    y = _linear_out(M, N, out_dtype or torch.float16, x.device, out)
+    need = _lib.paro_workspace_bytes(M, D, N)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(_lib.paro_w4a16_linear(M, D, N, _ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), _ydt(y),
+                                      _ptr(ws), ws.numel() if ws is not None else 0, _stream_ptr(x.device)),
+               "paro_w4a16_linear")
+    return y
+
+
+def paro_rotated_linear(rot: Rotation, x, qweight, scales, zeros, out_dtype=None, out=None, ws=None):
+    """Fused runtime path: y = transform(x) . dequant(qweight, scales, zeros)^T."""
+    torch = _torch()
+    M, D = int(x.shape[0]), rot.D
+    N = int(qweight.shape[0])
+    _want(x, torch.float16, (M, D), "x")
+    _want(qweight, torch.uint8, (N, D // 2), "qweight")
+    _want(scales, torch.float16, (N, D // GROUP), "scales")
+    _want(zeros, torch.float16, (N, D // GROUP), "zeros")
+    y = _linear_out(M, N, out_dtype or torch.float16, x.device, out)
+    need = _lib.paro_workspace_bytes(M, D, N)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(_lib.paro_rotated_linear(rot.ptr, M, N, _ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y),
+                                        _ydt(y), _ptr(ws), ws.numel() if ws is not None else 0,
+                                        _stream_ptr(x.device)),
+               "paro_rotated_linear")
+    return y

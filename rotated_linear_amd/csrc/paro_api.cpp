@@ -1,0 +1,211 @@
+// Host side of libparo: argument validation, descriptor preparation and dispatch.
+// Every error path returns before anything is enqueued on the stream.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "paro_internal.h"
+
+using namespace paro;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+paro_status check_shape(int K, int D) {
+  if (D < PARO_GROUP || D > PARO_MAX_D || (D % PARO_GROUP) != 0) return PARO_ESHAPE;
+  if (K < 0 || K > PARO_MAX_K) return PARO_ESHAPE;
+  return PARO_OK;
+}
+
+paro_status check_rotation(const paro_rotation* r) {
+  if (!r || !r->dev) return PARO_EINVAL;
+  if (check_shape(r->K, r->D) != PARO_OK) return PARO_ESHAPE;
+  if (!aligned16(r->dev)) return PARO_EINVAL;
+  return PARO_OK;
+}
+
+paro_status from_hip(hipError_t e) { return e == hipSuccess ? PARO_OK : PARO_EHIP; }
+
+size_t linear_ws_bytes(bool rotated, int M, int D) {
+  if (!rotated || M <= 0 || fused_decode_ok(M, D)) return 0;
+  return align256(size_t(M) * size_t(D) * 2);
+}
+
+paro_status check_linear_args(int M, int D, int N, const void* x, const uint8_t* qweight,
+                              const void* scales, const void* zeros, void* y, int ydtype) {
+  if (M < 0 || N < 0) return PARO_EINVAL;
+  if (ydtype != PARO_F16 && ydtype != PARO_F32) return PARO_EINVAL;
+  if (M == 0 || N == 0) return PARO_OK;
+  if (!x || !qweight || !scales || !zeros || !y) return PARO_EINVAL;
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(y)) return PARO_EINVAL;
+  // scales/zeros rows are D/128 halves long; only 2-byte alignment is needed.
+  if ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 1u) return PARO_EINVAL;
+  const size_t ybytes = size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2);
+  const size_t G = size_t(D / PARO_GROUP);
+  if (overlap(y, ybytes, x, size_t(M) * D * 2) || overlap(y, ybytes, qweight, size_t(N) * D / 2) ||
+      overlap(y, ybytes, scales, size_t(N) * G * 2) || overlap(y, ybytes, zeros, size_t(N) * G * 2))
+    return PARO_EINVAL;
+  return PARO_OK;
+}
+
+}  // namespace
+
+bool paro::fused_decode_ok(int M, int D) {
+  // rotation buffer (float32 [D][M]) + transformed activations (float16 [M][D]) in LDS
+  const int mr = M == 1 ? 1 : (M == 2 ? 2 : 4);  // rows the kernel instance holds
+  return M >= 1 && M <= kFusedMaxM && size_t(mr) * size_t(D) * 6 <= 96u * 1024u;
+}
+
+extern "C" {
+
+const char* paro_status_str(int status) {
+  switch (status) {
+    case PARO_OK: return "PARO_OK";
+    case PARO_EINVAL: return "PARO_EINVAL: invalid argument (null/misaligned pointer, negative size, dtype or aliasing)";
+    case PARO_ESHAPE: return "PARO_ESHAPE: D must be a multiple of 128 in [128, 16384] and K in [0, 64]";
+    case PARO_EPAIRS: return "PARO_EPAIRS: a stage does not pair every channel exactly once";
+    case PARO_ESCALE: return "PARO_ESCALE: channel scales must be finite and > 0, angles finite";
+    case PARO_EWORKSPACE: return "PARO_EWORKSPACE: workspace smaller than paro_workspace_bytes()";
+    case PARO_EHIP: return "PARO_EHIP: HIP runtime error";
+    default: return "PARO_UNKNOWN";
+  }
+}
+
+int paro_version(void) { return 100; }
+
+size_t paro_rotation_bytes(int K, int D) {
+  if (check_shape(K, D) != PARO_OK) return 0;
+  return desc_layout(K, D).total;
+}
+
+paro_status paro_rotation_prepare(int K, int D, const int32_t* pairs_host, const float* theta_host,
+                                  const float* scale_host, void* desc_dev, size_t desc_bytes,
+                                  paro_rotation* out, void* stream) {
+  if (!out || !desc_dev || !scale_host || (K > 0 && (!pairs_host || !theta_host))) return PARO_EINVAL;
+  if (paro_status s = check_shape(K, D)) return s;
+  if (!aligned16(desc_dev)) return PARO_EINVAL;
+  const DescLayout L = desc_layout(K, D);
+  if (desc_bytes < L.total) return PARO_EINVAL;
+  const int P = D / 2;
+
+  std::vector<unsigned char> host(L.total, 0);
+  uint32_t* pr = reinterpret_cast<uint32_t*>(host.data() + L.pairs_off);
+  float* cs = reinterpret_cast<float*>(host.data() + L.cs_off);
+  float* inv_s = reinterpret_cast<float*>(host.data() + L.inv_s_off);
+  float* s = reinterpret_cast<float*>(host.data() + L.s_off);
+
+  std::vector<int> seen(D);
+  for (int k = 0; k < K; ++k) {
+    std::fill(seen.begin(), seen.end(), 0);
+    for (int p = 0; p < P; ++p) {
+      const int32_t i = pairs_host[(size_t(k) * P + p) * 2 + 0];
+      const int32_t j = pairs_host[(size_t(k) * P + p) * 2 + 1];
+      if (i < 0 || i >= D || j < 0 || j >= D || i == j || seen[i] || seen[j]) return PARO_EPAIRS;
+      seen[i] = seen[j] = 1;
+      const float t = theta_host[size_t(k) * P + p];
+      if (!isfinite(t)) return PARO_ESCALE;
+      pr[size_t(k) * P + p] = uint32_t(i) | (uint32_t(j) << 16);
+      cs[(size_t(k) * P + p) * 2 + 0] = static_cast<float>(cos(static_cast<double>(t)));
+      cs[(size_t(k) * P + p) * 2 + 1] = static_cast<float>(sin(static_cast<double>(t)));
+    }
+  }
+  for (int c = 0; c < D; ++c) {
+    const float v = scale_host[c];
+    if (!isfinite(v) || !(v > 0.0f)) return PARO_ESCALE;
+    s[c] = v;
+    inv_s[c] = static_cast<float>(1.0 / static_cast<double>(v));
+    if (!isfinite(inv_s[c]) || inv_s[c] == 0.0f) return PARO_ESCALE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(desc_dev, host.data(), L.total, hipMemcpyHostToDevice, st) != hipSuccess) return PARO_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return PARO_EHIP;
+  out->K = K;
+  out->D = D;
+  out->dev = desc_dev;
+  return PARO_OK;
+}
+
+paro_status paro_pack_weights(const paro_rotation* r, int N, const void* W, uint8_t* qweight, void* scales,
+                              void* zeros, void* stream) {
+  if (paro_status s = check_rotation(r)) return s;
+  if (N < 0) return PARO_EINVAL;
+  if (N == 0) return PARO_OK;
+  if (!W || !qweight || !scales || !zeros) return PARO_EINVAL;
+  if (!aligned16(W) || !aligned16(qweight)) return PARO_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 1u) return PARO_EINVAL;
+  const size_t D = size_t(r->D), G = D / PARO_GROUP;
+  const size_t wb = size_t(N) * D * 2;
+  if (overlap(W, wb, qweight, size_t(N) * D / 2) || overlap(W, wb, scales, size_t(N) * G * 2) ||
+      overlap(W, wb, zeros, size_t(N) * G * 2) || overlap(scales, size_t(N) * G * 2, zeros, size_t(N) * G * 2))
+    return PARO_EINVAL;
+  return from_hip(launch_pack(dev_rot(*r), N, static_cast<const uint16_t*>(W), qweight,
+                              static_cast<uint16_t*>(scales), static_cast<uint16_t*>(zeros),
+                              static_cast<hipStream_t>(stream)));
+}
+
+paro_status paro_rotate(const paro_rotation* r, int M, const void* x, void* xout, void* stream) {
+  if (paro_status s = check_rotation(r)) return s;
+  if (M < 0) return PARO_EINVAL;
+  if (M == 0) return PARO_OK;
+  if (!x || !xout || !aligned16(x) || !aligned16(xout)) return PARO_EINVAL;
+  const size_t bytes = size_t(M) * size_t(r->D) * 2;
+  if (overlap(x, bytes, xout, bytes)) return PARO_EINVAL;
+  return from_hip(launch_rotate(dev_rot(*r), M, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xout),
+                                static_cast<hipStream_t>(stream)));
+}
+
+size_t paro_workspace_bytes(int M, int D, int N) {
+  (void)N;
+  if (M <= 0 || check_shape(0, D) != PARO_OK) return 0;
+  return linear_ws_bytes(true, M, D);
+}
+
+static paro_status run_linear(int M, int D, int N, const uint16_t* x, const uint8_t* qweight,
+                              const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, hipStream_t st) {
+  if (M <= kGemvMaxM) return from_hip(launch_gemv(nullptr, M, D, N, x, qweight, scales, zeros, y, ydtype, st));
+  return from_hip(launch_gemm(M, D, N, x, qweight, scales, zeros, y, ydtype, st));
+}
+
+paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t* qweight, const void* scales,
+                              const void* zeros, void* y, int ydtype, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (paro_status s = check_shape(0, D)) return s;
+  if (paro_status s = check_linear_args(M, D, N, x, qweight, scales, zeros, y, ydtype)) return s;
+  if (M == 0 || N == 0) return PARO_OK;
+  return run_linear(M, D, N, static_cast<const uint16_t*>(x), qweight, static_cast<const uint16_t*>(scales),
+                    static_cast<const uint16_t*>(zeros), y, ydtype, static_cast<hipStream_t>(stream));
+}
+
+paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void* x, const uint8_t* qweight,
+                                const void* scales, const void* zeros, void* y, int ydtype, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (paro_status s = check_rotation(r)) return s;
+  const int D = r->D;
+  if (paro_status s = check_linear_args(M, D, N, x, qweight, scales, zeros, y, ydtype)) return s;
+  if (M == 0 || N == 0) return PARO_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const DevRot R = dev_rot(*r);
+  if (fused_decode_ok(M, D))
+    return from_hip(launch_gemv(&R, M, D, N, static_cast<const uint16_t*>(x), qweight,
+                                static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), y,
+                                ydtype, st));
+  const size_t need = linear_ws_bytes(true, M, D);
+  if (!ws || ws_bytes < need) return PARO_EWORKSPACE;
+  if (!aligned16(ws)) return PARO_EINVAL;
+  const size_t ybytes = size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2);
+  if (overlap(ws, need, x, size_t(M) * D * 2) || overlap(ws, need, y, ybytes)) return PARO_EINVAL;
+  uint16_t* xr = static_cast<uint16_t*>(ws);
+  if (hipError_t e = launch_rotate(R, M, static_cast<const uint16_t*>(x), xr, st)) return from_hip(e);
+  return run_linear(M, D, N, xr, qweight, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
+                    y, ydtype, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before any HIP call is made.
+
+Pointers handed to the library here are fake (never dereferenced): every case
+returns from host-side validation before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paro.h")
+
+rl = pytest.importorskip("rotated_linear_amd", reason="libparo.so not built")
+lib = rl.lib()
+P = ctypes.POINTER(rl.paro_rotation)
+FAKE = 0x100000  # 16-byte aligned, never dereferenced on these paths
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(paro_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    out = subprocess.run(["nm", "-D", "--defined-only", rl.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(paro_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib, n)
+    assert set(names) == set(rl.EXPORTS)
+
+
+def test_status_strings_and_sizes():
+    for s in range(7):
+        assert lib.paro_status_str(s).decode().startswith(rl.STATUS[s])
+    assert lib.paro_status_str(99) == b"PARO_UNKNOWN"
+    assert lib.paro_version() >= 100
+    # descriptor: pairs (4 B) + cos/sin (8 B) per pair per stage + 1/s and s (4 B each) per channel,
+    # each section padded to 256 bytes
+    assert rl.paro_rotation_bytes(8, 1536) == 8 * 768 * 4 + 8 * 768 * 8 + 2 * 1536 * 4
+    assert rl.paro_rotation_bytes(0, 128) == 2 * 512
+    for K, D in ((8, 100), (8, 1537), (-1, 256), (65, 256), (2, 16512), (2, 0)):
+        assert rl.paro_rotation_bytes(K, D) == 0, (K, D)
+    assert rl.paro_workspace_bytes(1, 1536, 1536) == 0  # fused decode path
+    assert rl.paro_workspace_bytes(64, 4096, 4096) == 64 * 4096 * 2
+    assert rl.paro_workspace_bytes(0, 4096, 4096) == 0
+
+
+def _prep(K, D, pairs, theta, scale, desc=FAKE, nbytes=1 << 30, out=True):
+    h = rl.paro_rotation()
+    return lib.paro_rotation_prepare(K, D, pairs.ctypes.data_as(ctypes.c_void_p) if pairs is not None else None,
+                                     theta.ctypes.data_as(ctypes.c_void_p) if theta is not None else None,
+                                     scale.ctypes.data_as(ctypes.c_void_p) if scale is not None else None,
+                                     desc, nbytes, ctypes.byref(h) if out else None, None)
+
+
+def _good(K=2, D=256, seed=0):
+    rng = np.random.default_rng(seed)
+    pairs = np.stack([rng.permutation(D).reshape(D // 2, 2) for _ in range(K)]).astype(np.int32)
+    theta = rng.uniform(-3, 3, (K, D // 2)).astype(np.float32)
+    scale = np.exp(rng.normal(0, 0.3, D)).astype(np.float32)
+    return pairs, theta, scale
+
+
+def test_prepare_rejects_bad_matchings():
+    pairs, theta, scale = _good()
+    dup = pairs.copy()
+    dup[1, 5, 0] = dup[1, 6, 1]  # channel used twice in stage 1, another one missing
+    assert _prep(2, 256, dup, theta, scale) == 3
+    oor = pairs.copy()
+    oor[0, 0, 1] = 256
+    assert _prep(2, 256, oor, theta, scale) == 3
+    neg = pairs.copy()
+    neg[0, 3, 0] = -1
+    assert _prep(2, 256, neg, theta, scale) == 3
+    self_pair = pairs.copy()
+    self_pair[0, 0, 1] = self_pair[0, 0, 0]
+    assert _prep(2, 256, self_pair, theta, scale) == 3
+
+
+def test_prepare_rejects_bad_scales_and_angles():
+    pairs, theta, scale = _good()
+    for bad in (0.0, -1.0, np.inf, np.nan):
+        s = scale.copy()
+        s[17] = bad
+        assert _prep(2, 256, pairs, theta, s) == 4, bad
+    t = theta.copy()
+    t[1, 3] = np.nan
+    assert _prep(2, 256, pairs, t, scale) == 4
+    s = scale.copy()
+    s[0] = 1e-45  # 1/s overflows float32
+    assert _prep(2, 256, pairs, theta, s) == 4
+
+
+def test_prepare_rejects_bad_shapes_and_pointers():
+    pairs, theta, scale = _good()
+    assert _prep(2, 200, pairs, theta, scale) == 2
+    assert _prep(2, 255, pairs, theta, scale) == 2
+    assert _prep(65, 256, pairs, theta, scale) == 2
+    assert _prep(2, 256, pairs, theta, scale, desc=None) == 1
+    assert _prep(2, 256, pairs, theta, scale, desc=FAKE + 8) == 1  # misaligned
+    assert _prep(2, 256, pairs, theta, scale, nbytes=100) == 1  # descriptor too small
+    assert _prep(2, 256, pairs, theta, scale, out=False) == 1
+    assert _prep(2, 256, None, theta, scale) == 1
+
+
+def _rot(K=2, D=256, dev=FAKE):
+    return rl.paro_rotation(K, D, dev)
+
+
+def test_calls_reject_bad_arguments_before_launch():
+    r = _rot()
+    v = ctypes.c_void_p
+    # pack
+    assert lib.paro_pack_weights(None, 4, v(FAKE), v(FAKE * 2), v(FAKE * 3), v(FAKE * 4), None) == 1
+    assert lib.paro_pack_weights(ctypes.byref(r), -1, v(FAKE), v(FAKE * 2), v(FAKE * 3), v(FAKE * 4), None) == 1
+    assert lib.paro_pack_weights(ctypes.byref(r), 0, None, None, None, None, None) == 0  # nothing to do
+    assert lib.paro_pack_weights(ctypes.byref(r), 4, v(FAKE), v(FAKE), v(FAKE * 3), v(FAKE * 4), None) == 1  # alias
+    bad_shape = _rot(2, 250)
+    assert lib.paro_pack_weights(ctypes.byref(bad_shape), 4, v(FAKE), v(FAKE * 2), v(FAKE * 3), v(FAKE * 4), None) == 2
+    misaligned = _rot(2, 256, FAKE + 4)
+    assert lib.paro_rotate(ctypes.byref(misaligned), 4, v(FAKE), v(FAKE * 2), None) == 1
+    # rotate
+    assert lib.paro_rotate(ctypes.byref(r), 0, None, None, None) == 0
+    assert lib.paro_rotate(ctypes.byref(r), -2, v(FAKE), v(FAKE * 2), None) == 1
+    assert lib.paro_rotate(ctypes.byref(r), 4, v(FAKE), v(FAKE + 256), None) == 1  # overlapping in/out
+    assert lib.paro_rotate(ctypes.byref(r), 4, v(FAKE + 2), v(FAKE * 2), None) == 1  # misaligned
+    # plain linear
+    args = (v(FAKE), v(FAKE * 2), v(FAKE * 3), v(FAKE * 4))
+    assert lib.paro_w4a16_linear(4, 256, 64, *args, v(FAKE * 5), 7, None, 0, None) == 1  # dtype
+    assert lib.paro_w4a16_linear(4, 250, 64, *args, v(FAKE * 5), 0, None, 0, None) == 2  # D
+    assert lib.paro_w4a16_linear(4, 256, 64, *args, v(FAKE), 0, None, 0, None) == 1  # y aliases x
+    assert lib.paro_w4a16_linear(0, 256, 64, *args, v(FAKE * 5), 0, None, 0, None) == 0  # empty
+    assert lib.paro_w4a16_linear(4, 256, 0, *args, v(FAKE * 5), 0, None, 0, None) == 0  # empty
+    assert lib.paro_w4a16_linear(-1, 256, 64, *args, v(FAKE * 5), 0, None, 0, None) == 1
+    assert lib.paro_w4a16_linear(4, 256, 64, None, *args[1:], v(FAKE * 5), 0, None, 0, None) == 1
+    assert lib.paro_w4a16_linear(4, 256, 64, *args[:2], v(FAKE * 3 + 1), args[3], v(FAKE * 5), 0, None, 0,
+                                 None) == 1  # odd scales pointer
+    # rotated linear: large M needs a workspace
+    big = _rot(8, 4096)
+    assert rl.paro_workspace_bytes(64, 4096, 512) > 0
+    assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, None, 0, None) == 5
+    assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, v(FAKE * 6), 100, None) == 5
+    assert lib.paro_rotated_linear(None, 1, 512, *args, v(FAKE * 5), 0, None, 0, None) == 1

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars:
+  * pack: qweight bytes, scales and zeros bit-identical to the oracle;
+  * rotate: every element within ``rotate_bound`` of the float64 transform, and at
+    most 2% of elements off the float16 rounding of the float64 transform;
+  * linears (spec bar): max-abs <= 1e-2 and relative L2 <= 2e-3, with the
+    float32-output epilogue, against the oracle applied to the same dequantized
+    weights and -- for the rotated linear -- the same float16 activations the
+    GEMM consumes (f16_rne of the float64 transform); the production float16
+    output is also held to relative L2 <= 2e-3 against the unrounded float64 path.
+Full-size workloads are checked on sampled weight rows / token rows, always
+including the first and last (ragged) ones.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+rl = pytest.importorskip("rotated_linear_amd")
+
+
+def _rot(L):
+    return rl.paro_rotation_prepare(L.pairs, L.theta, L.scale)
+
+
+# --------------------------------------------------------------------------- #
+# pack: bit-exact
+# --------------------------------------------------------------------------- #
+
+PACK_CASES = [(1, 0), (2, 0), (2, 1), (3, 0), (4, 0)] + [(5, i) for i in range(7)]
+
+
+@pytest.mark.parametrize("wid,index", PACK_CASES)
+def test_pack_bitexact(wid, index):
+    L = C.linear_inputs(wid, index)
+    C.log(f"pack wid={wid} linear={L.spec.name} N={L.spec.N} D={L.spec.D} K={L.spec.K}")
+    rot = _rot(L)
+    qw, sc, z = rl.paro_pack_weights(rot, C.dev(L.W, torch))
+    torch.cuda.synchronize()
+    rows = C.sample_rows(L.spec.N, 384, seed=wid * 10 + index)
+    key = None if len(rows) == L.spec.N else tuple(int(r) for r in rows)
+    oq, osc, oz = C.oracle_pack_rows(wid, index, key)
+    gq, gsc, gz = C.host(qw)[rows], C.host(sc)[rows], C.host(z)[rows]
+    assert np.array_equal(gq, oq), f"qweight differs in {(gq != oq).sum()} bytes"
+    assert np.array_equal(gsc.view(np.uint16), osc.view(np.uint16)), "scales differ"
+    assert np.array_equal(gz.astype(np.float64), oz.astype(np.float64)), "zeros differ"
+
+
+def test_pack_pair_order_and_roles_do_not_matter():
+    """Disjoint pairs: reordering the pairs of a stage, or swapping (i, j) with theta -> -theta,
+    leaves the folded weights bit-identical (section "A rotation small enough to execute")."""
+    L = W.custom_linear(31, 1, 512, 96, 4)
+    C.log("pack pair order / role swap D=512 N=96 K=4")
+    rng = np.random.default_rng(5)
+    pairs2, theta2 = L.pairs.copy(), L.theta.copy()
+    for k in range(L.pairs.shape[0]):
+        perm = rng.permutation(L.pairs.shape[1])
+        pairs2[k], theta2[k] = pairs2[k][perm], theta2[k][perm]
+        flip = rng.random(L.pairs.shape[1]) < 0.5
+        pairs2[k][flip] = pairs2[k][flip][:, ::-1]
+        theta2[k][flip] = -theta2[k][flip]
+    Wd = C.dev(L.W, torch)
+    a = [C.host(t) for t in rl.paro_pack_weights(_rot(L), Wd)]
+    b = [C.host(t) for t in rl.paro_pack_weights(rl.paro_rotation_prepare(pairs2, theta2, L.scale), Wd)]
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_pack_edge_shapes():
+    for (M, D, N, K) in ((1, 128, 1, 0), (1, 128, 3, 1), (1, 16384, 2, 2), (1, 640, 33, 8)):
+        L = W.custom_linear(7, M, D, N, K)
+        C.log(f"pack edge D={D} N={N} K={K}")
+        qw, sc, z = rl.paro_pack_weights(_rot(L), C.dev(L.W, torch))
+        oq, osc, oz = O.pack_weights(L.W, L.pairs, L.theta, L.scale)
+        assert np.array_equal(C.host(qw), oq)
+        assert np.array_equal(C.host(sc).view(np.uint16), osc.view(np.uint16))
+        assert np.array_equal(C.host(z).astype(np.float64), oz.astype(np.float64))
+
+
+# --------------------------------------------------------------------------- #
+# rotate
+# --------------------------------------------------------------------------- #
+
+def _check_rotate(L, x):
+    rot = _rot(L)
+    got = C.host(rl.paro_rotate(rot, C.dev(x, torch))).astype(np.float64)
+    a = O.transform_activations(x, L.pairs, L.theta, L.scale)
+    bound = C.rotate_bound(a, x.astype(np.float64), L.scale, L.spec.K)
+    err = np.abs(got - a)
+    worst = float((err / bound).max())
+    assert worst <= 1.0, f"rotate error {worst:.3f}x the bound"
+    off = float((got != O.f16_rne(a).astype(np.float64)).mean())
+    assert off <= 0.02, f"{off:.4%} of elements off the float16 rounding of the float64 transform"
+    return got
+
+
+ROT_CASES = [(1, 0, 4), (2, 0, 1), (2, 1, 4), (2, 3, 16), (3, 0, 1), (3, 0, 16), (3, 0, 256), (4, 0, 2048),
+             (5, 0, 64), (5, 6, 64), (5, 4, 4096)]
+
+
+@pytest.mark.parametrize("wid,index,M", ROT_CASES)
+def test_rotate_parity(wid, index, M):
+    L = C.linear_inputs(wid, index)
+    C.log(f"rotate wid={wid} linear={L.spec.name} M={M} D={L.spec.D} K={L.spec.K}")
+    x = L.x[:M]
+    if M > 512:  # full-size batch: compare a row sample (rows are independent)
+        rot = _rot(L)
+        got = C.host(rl.paro_rotate(rot, C.dev(x, torch))).astype(np.float64)
+        rows = C.sample_rows(M, 128, seed=M)
+        a = O.transform_activations(x[rows], L.pairs, L.theta, L.scale)
+        bound = C.rotate_bound(a, x[rows].astype(np.float64), L.scale, L.spec.K)
+        assert float((np.abs(got[rows] - a) / bound).max()) <= 1.0
+    else:
+        _check_rotate(L, x)
+
+
+def test_rotate_identity_and_order():
+    L = W.custom_linear(3, 5, 384, 8, 3)
+    C.log("rotate identity / pair-order shuffle D=384 M=5")
+    zero = np.zeros_like(L.theta)
+    ones = np.ones_like(L.scale)
+    xd = C.dev(L.x, torch)
+    same = C.host(rl.paro_rotate(rl.paro_rotation_prepare(L.pairs, zero, ones), xd))
+    assert np.array_equal(same.view(np.uint16), L.x.view(np.uint16)), "theta=0, s=1 must be the identity"
+    base = C.host(rl.paro_rotate(_rot(L), xd))
+    rng = np.random.default_rng(9)
+    p2, t2 = L.pairs.copy(), L.theta.copy()
+    for k in range(L.pairs.shape[0]):
+        perm = rng.permutation(L.pairs.shape[1])
+        p2[k], t2[k] = p2[k][perm], t2[k][perm]
+    shuf = C.host(rl.paro_rotate(rl.paro_rotation_prepare(p2, t2, L.scale), xd))
+    assert np.array_equal(base.view(np.uint16), shuf.view(np.uint16)), "pair order within a stage changed bits"
+    again = C.host(rl.paro_rotate(_rot(L), xd))
+    assert np.array_equal(base.view(np.uint16), again.view(np.uint16)), "not deterministic"
+
+
+@pytest.mark.parametrize("M,D,K", [(1, 128, 0), (3, 128, 1), (5, 384, 3), (7, 16384, 2), (9, 1280, 8),
+                                   (130, 640, 5)])
+def test_rotate_edge_shapes(M, D, K):
+    L = W.custom_linear(11, M, D, 4, K)
+    C.log(f"rotate edge M={M} D={D} K={K}")
+    _check_rotate(L, L.x)
+
+
+# --------------------------------------------------------------------------- #
+# linears
+# --------------------------------------------------------------------------- #
+
+def _linear_case(L, M, rows_w, oracle_pack, gpu_weights):
+    """Run both linears on the GPU and compare against the oracle on the sampled weight rows."""
+    x = L.x[:M]
+    xd = C.dev(x, torch)
+    rot = _rot(L)
+    qw, sc, z = gpu_weights
+    y32 = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z, out_dtype=torch.float32))
+    y16 = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z, out_dtype=torch.float16))
+    p32 = C.host(rl.paro_w4a16_linear(xd, qw, sc, z, out_dtype=torch.float32))
+    oq, osc, oz = oracle_pack
+    a = O.transform_activations(x, L.pairs, L.theta, L.scale)
+    deq = O.dequantize(oq, osc, oz)
+    ref_fused = O.f16_rne(a).astype(np.float64) @ deq.T
+    ref_exact = a @ deq.T
+    ref_plain = x.astype(np.float64) @ deq.T
+    mx, rel = C.linear_metrics(y32[:, rows_w], ref_fused)
+    assert mx <= C.MAX_ABS and rel <= C.REL_L2, f"rotated linear (fp32 out): max-abs {mx:.3e} rel-L2 {rel:.3e}"
+    mx2, rel2 = C.linear_metrics(y16[:, rows_w], ref_exact)
+    assert rel2 <= C.REL_L2, f"rotated linear (fp16 out vs float64 path): rel-L2 {rel2:.3e} (max-abs {mx2:.3e})"
+    mx3, rel3 = C.linear_metrics(p32[:, rows_w], ref_plain)
+    assert mx3 <= C.MAX_ABS and rel3 <= C.REL_L2, f"w4a16 linear: max-abs {mx3:.3e} rel-L2 {rel3:.3e}"
+    return mx, rel, mx2, rel2
+
+
+LIN_CASES = [(1, 0, 4), (2, 0, 1), (2, 0, 4), (2, 0, 16), (2, 1, 1), (2, 1, 16), (2, 3, 4), (3, 0, 1), (3, 0, 16),
+             (3, 0, 256), (4, 0, 2048), (5, 0, 64), (5, 1, 64), (5, 4, 64), (5, 6, 64), (5, 3, 4096), (5, 6, 4096)]
+
+
+@pytest.mark.parametrize("wid,index,M", LIN_CASES)
+def test_linear_parity(wid, index, M):
+    L = C.linear_inputs(wid, index)
+    C.log(f"linear wid={wid} linear={L.spec.name} M={M} N={L.spec.N} D={L.spec.D}")
+    N = L.spec.N
+    rows_w = C.sample_rows(N, 256, seed=wid * 100 + index)
+    key = None if len(rows_w) == N else tuple(int(r) for r in rows_w)
+    oracle_pack = C.oracle_pack_rows(wid, index, key)
+    if key is None:
+        gpu_w = tuple(C.dev(t, torch) for t in oracle_pack)  # the oracle's own packed weights
+    else:
+        gpu_w = rl.paro_pack_weights(_rot(L), C.dev(L.W, torch))  # full weights; sampled rows checked bit-exact
+        assert np.array_equal(C.host(gpu_w[0])[rows_w], oracle_pack[0])
+    if M > 512:  # token-row sample for the large prefill batches
+        Lm = L
+        x_rows = C.sample_rows(M, 96, seed=M + index)
+        x = L.x[:M]
+        xd = C.dev(x, torch)
+        rot = _rot(L)
+        y32 = C.host(rl.paro_rotated_linear(rot, xd, *gpu_w, out_dtype=torch.float32))[x_rows][:, rows_w]
+        p32 = C.host(rl.paro_w4a16_linear(xd, *gpu_w, out_dtype=torch.float32))[x_rows][:, rows_w]
+        a = O.transform_activations(x[x_rows], Lm.pairs, Lm.theta, Lm.scale)
+        deq = O.dequantize(*oracle_pack)
+        mx, rel = C.linear_metrics(y32, O.f16_rne(a).astype(np.float64) @ deq.T)
+        assert mx <= C.MAX_ABS and rel <= C.REL_L2, f"rotated linear: max-abs {mx:.3e} rel-L2 {rel:.3e}"
+        mx3, rel3 = C.linear_metrics(p32, x[x_rows].astype(np.float64) @ deq.T)
+        assert mx3 <= C.MAX_ABS and rel3 <= C.REL_L2, f"w4a16 linear: max-abs {mx3:.3e} rel-L2 {rel3:.3e}"
+        C.log(f"  max-abs {mx:.2e} rel-L2 {rel:.2e}")
+    else:
+        mx, rel, _, _ = _linear_case(L, M, rows_w, oracle_pack, gpu_w)
+        C.log(f"  max-abs {mx:.2e} rel-L2 {rel:.2e}")
+
+
+@pytest.mark.parametrize("M,D,N,K", [(1, 128, 1, 1), (2, 384, 200, 3), (3, 640, 77, 2), (4, 256, 513, 0),
+                                     (5, 384, 200, 3), (17, 1280, 130, 4), (33, 512, 64, 2), (65, 768, 96, 8),
+                                     (130, 1024, 300, 5), (257, 384, 129, 1), (1, 16384, 40, 2), (6, 16384, 20, 2)])
+def test_linear_edge_shapes(M, D, N, K):
+    L = W.custom_linear(21, M, D, N, K)
+    C.log(f"linear edge M={M} D={D} N={N} K={K}")
+    op = O.pack_weights(L.W, L.pairs, L.theta, L.scale)
+    _linear_case(L, M, np.arange(N), op, tuple(C.dev(t, torch) for t in op))
+
+
+@pytest.mark.parametrize("M", [1, 3, 4, 16, 200])
+def test_identity_transform_matches_plain_linear(M):
+    """K = 0 with s = 1: the rotated linear must equal the plain INT4 linear bit for bit."""
+    L = W.custom_linear(41, M, 1536, 300, 0)
+    C.log(f"identity transform M={M}")
+    rot = rl.paro_rotation_prepare(L.pairs, L.theta, np.ones_like(L.scale))
+    qw, sc, z = rl.paro_pack_weights(rot, C.dev(L.W, torch))
+    xd = C.dev(L.x, torch)
+    for dt in (torch.float16, torch.float32):
+        a = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z, out_dtype=dt))
+        b = C.host(rl.paro_w4a16_linear(xd, qw, sc, z, out_dtype=dt))
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_empty_inputs_are_noops():
+    L = W.custom_linear(2, 1, 256, 8, 1)
+    C.log("empty inputs")
+    rot = _rot(L)
+    x0 = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    assert rl.paro_rotate(rot, x0).shape == (0, 256)
+    qw, sc, z = rl.paro_pack_weights(rot, C.dev(L.W, torch))
+    y = torch.full((0, 8), 7.0, dtype=torch.float16, device="cuda")
+    rl.paro_rotated_linear(rot, x0, qw, sc, z, out=y)
+    sentinel = torch.full((1, 0), 7.0, dtype=torch.float16, device="cuda")
+    rl.paro_w4a16_linear(C.dev(L.x, torch), qw[:0], sc[:0], z[:0], out=sentinel)
+    torch.cuda.synchronize()
+
+
+def test_workspace_and_determinism():
+    L = C.linear_inputs(4, 0)
+    C.log("workspace / determinism down_proj M=300")
+    rot = _rot(L)
+    qw, sc, z = rl.paro_pack_weights(rot, C.dev(L.W, torch))
+    xd = C.dev(L.x[:300], torch)
+    need = rl.paro_workspace_bytes(300, L.spec.D, L.spec.N)
+    assert need >= 300 * L.spec.D * 2
+    with pytest.raises(rl.ParoError):
+        rl.paro_rotated_linear(rot, xd, qw, sc, z, ws=torch.empty(need - 256, dtype=torch.uint8, device="cuda"))
+    a = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z))
+    b = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z,
+                                      ws=torch.empty(need + 4096, dtype=torch.uint8, device="cuda")))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
