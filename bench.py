@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated W4A16 linear on one MI355X.
+
+Workload (default): the Qwen2.5-1.5B-shaped attention projections in decode --
+q, k, v, o (D=1536 -> N=1536/256/256/1536), K=8 Givens stages, INT4 group 128 --
+at M = 1, 4 and 16 tokens. One step = the 12 fused rotated linears (4 linears x
+3 batch sizes), each reading its weights, scales, zeros and transform
+descriptor cold from HBM: every call takes the next copy from a pool larger
+than 1 GiB (four times the 256 MB Infinity Cache). Steps are replayed as HIP
+graphs captured from the library's own launches, so Python call overhead stays
+out of the timed region.
+
+Prints ONE JSON line: decode HBM GB/s of the whole step (algorithmic bytes /
+time), the roofline of the dominant kernel, the CPU oracle's throughput on a
+bounded sample, the rotation overhead against the plain INT4 linear on the same
+step, and prefill / large-decode extras (gate+up decode, down_proj prefill).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "rotated W4A16 linear: decode HBM GB/s, prefill TFLOP/s, rotation overhead %"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+POOL_BYTES = int(1.1 * (1 << 30))
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-extras", action="store_true", help="skip the gate+up / down_proj extras")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+# --------------------------------------------------------------------------- #
+# building blocks
+# --------------------------------------------------------------------------- #
+
+class Linear:
+    """One linear's prepared transform and packed weights, plus pool copies for cold reads."""
+
+    def __init__(self, rl, torch, L):
+        self.L = L
+        self.D, self.N, self.K = L.spec.D, L.spec.N, L.spec.K
+        self.rot = rl.paro_rotation_prepare(L.pairs, L.theta, L.scale)
+        self.w = rl.paro_pack_weights(self.rot, torch.from_numpy(L.W).cuda())
+        self.copies = []
+
+    def set_bytes(self):
+        return sum(t.numel() * t.element_size() for t in self.w) + self.rot.desc.numel()
+
+    def make_copies(self, rl, n):
+        self.copies = []
+        for _ in range(n):
+            desc = self.rot.desc.clone()
+            rot = rl.Rotation(self.K, self.D, desc, rl.paro_rotation(self.K, self.D, desc.data_ptr()))
+            self.copies.append((rot, tuple(t.clone() for t in self.w)))
+
+
+def workload_bytes(M, D, N, K, rotated=True):
+    import workloads as W
+    return W.algorithmic_bytes(M, D, N, K) if rotated else W.plain_bytes(M, D, N)
+
+
+class Step:
+    """A list of (linear, M) calls; ``slot`` picks the pool copy used by the call."""
+
+    def __init__(self, rl, torch, linears, Ms):
+        self.rl, self.torch = rl, torch
+        self.linears, self.Ms = linears, Ms
+        self.calls = [(li, M) for M in Ms for li in range(len(linears))]
+        self.x = {}
+        self.y = {}
+        self.ws = {}
+        for li, M in self.calls:
+            lin = linears[li]
+            self.x[(li, M)] = torch.from_numpy(lin.L.x[:M]).cuda()
+            self.y[(li, M)] = torch.empty((M, lin.N), dtype=torch.float16, device="cuda")
+            need = rl.paro_workspace_bytes(M, lin.D, lin.N)
+            self.ws[(li, M)] = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+
+    def bytes(self, rotated=True):
+        return sum(workload_bytes(M, self.linears[li].D, self.linears[li].N, self.linears[li].K, rotated)
+                   for li, M in self.calls)
+
+    def flops(self):
+        return sum(2.0 * M * self.linears[li].D * self.linears[li].N for li, M in self.calls)
+
+    def enqueue(self, slot, rotated=True, only=None):
+        rl = self.rl
+        for ci, (li, M) in enumerate(self.calls):
+            if only is not None and ci not in only:
+                continue
+            lin = self.linears[li]
+            rot, w = lin.copies[(slot * len(self.Ms) + self.Ms.index(M)) % len(lin.copies)] if lin.copies \
+                else (lin.rot, lin.w)
+            if rotated:
+                rl.paro_rotated_linear(rot, self.x[(li, M)], *w, out=self.y[(li, M)], ws=self.ws[(li, M)])
+            else:
+                rl.paro_w4a16_linear(self.x[(li, M)], *w, out=self.y[(li, M)], ws=self.ws[(li, M)])
+
+
+def capture(torch, fn, n_graphs):
+    """Capture fn(slot) for slot in range(n_graphs) as separate HIP graphs."""
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)  # warm the kernels' one-time attributes outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for slot in range(n_graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(slot)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graphs(torch, graphs, steps, warmup):
+    """Replay graphs[t % len] for t < steps; returns ms per step (events bracket the K steps)."""
+    for t in range(warmup):
+        graphs[t % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for t in range(steps):
+        graphs[t % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+# --------------------------------------------------------------------------- #
+# CPU oracle baseline
+# --------------------------------------------------------------------------- #
+
+def cpu_baseline(step, seconds):
+    """The oracle's per-call path (float64 transform + x' . deq^T, deq precomputed) on the same
+    calls as a GPU step, repeated for about ``seconds`` of wall time."""
+    import numpy as np
+
+    import oracle as O
+
+    deq = {}
+    for li, lin in enumerate(step.linears):
+        qw, sc, z = (t.cpu().numpy() for t in lin.w)
+        deq[li] = O.dequantize(qw, sc, z)
+    xs = {k: v.cpu().numpy() for k, v in step.x.items()}
+    n_steps, t0 = 0, time.perf_counter()
+    while True:
+        for li, M in step.calls:
+            L = step.linears[li].L
+            a = O.transform_activations(xs[(li, M)], L.pairs, L.theta, L.scale)
+            _ = a @ deq[li].T
+        n_steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    gbs = step.bytes() * n_steps / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_steps} oracle passes over the step's {len(step.calls)} calls "
+                      f"(float64 transform + x'.deq^T, deq precomputed) in {el:.1f} s; "
+                      f"host {os.cpu_count()} logical CPUs, BLAS threads {cores}"}
+
+
+# --------------------------------------------------------------------------- #
+# main
+# --------------------------------------------------------------------------- #
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import rotated_linear_amd as rl
+    import workloads as W
+
+    torch.cuda.init()
+    wl = W.WORKLOADS[2]
+    linears = [Linear(rl, torch, W.make_linear(2, i)) for i in range(len(wl.linears))]
+    Ms = list(wl.Ms)
+    per_step_sets = len(Ms)
+    set_bytes = sum(l.set_bytes() for l in linears)
+    n_sets = max(4, math.ceil(POOL_BYTES / set_bytes))
+    for l in linears:
+        l.make_copies(rl, n_sets)
+    n_slots = max(1, n_sets // per_step_sets)
+    step = Step(rl, torch, linears, Ms)
+    torch.cuda.synchronize()
+
+    g_rot = capture(torch, lambda s: step.enqueue(s, rotated=True), n_slots)
+    ms_rot = time_graphs(torch, g_rot, args.steps, args.warmup)
+    g_plain = capture(torch, lambda s: step.enqueue(s, rotated=False), n_slots)
+    ms_plain = time_graphs(torch, g_plain, args.steps, args.warmup)
+
+    bytes_rot = step.bytes(True)
+    value = bytes_rot / (ms_rot * 1e-3) / 1e9
+    overhead = (ms_rot - ms_plain) / ms_plain * 100.0
+
+    # dominant kernel: the fused decode kernel on the q/o projection (the largest call class).
+    # Launch-only graphs of that one call over the cold pool give its average duration.
+    dom_ci = step.calls.index((0, 1))
+    g_dom = capture(torch, lambda s: [step.enqueue(s * 8 + r, rotated=True, only={dom_ci}) for r in range(8)],
+                    max(1, n_slots // 8))
+    ms_dom = time_graphs(torch, g_dom, max(8, args.steps // 4), 4) / 8
+    dom_bytes = workload_bytes(1, 1536, 1536, 8)
+    dom_gbs = dom_bytes / (ms_dom * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_kernel<FUSED=1,MR=1> (q proj, M=1, D=1536, N=1536)",
+                "avg_launch_us": round(ms_dom * 1e3, 3), "algorithmic_bytes_per_launch": dom_bytes}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_rot, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "Qwen2.5-1.5B attention projections q,k,v,o decode (D=1536; N=1536,256,256,1536)",
+                   "M": Ms, "K_stages": 8, "group": 128, "calls_per_step": len(step.calls),
+                   "algorithmic_bytes_per_step": bytes_rot, "cold_pool_bytes": set_bytes * n_sets,
+                   "launch": "HIP graph per step"},
+        "roofline": roofline,
+        "rotation_overhead_pct": round(overhead, 2),
+        "plain_w4a16": {"ms_per_step": round(ms_plain, 6),
+                        "GB/s": round(step.bytes(False) / (ms_plain * 1e-3) / 1e9, 3)},
+    }
+
+    if not args.no_extras:
+        out["extras"] = extras(rl, torch, W, args)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def extras(rl, torch, W, args):
+    """Larger shapes: gate+up decode (HBM) and down_proj prefill (MFMA), rotated vs plain."""
+    res = {}
+    L3 = Linear(rl, torch, W.make_linear(3, 0))
+    n3 = max(4, math.ceil(POOL_BYTES / L3.set_bytes()))
+    L3.make_copies(rl, n3)
+    for M in (1, 16):
+        st = Step(rl, torch, [L3], [M])
+        gr = capture(torch, lambda s: st.enqueue(s), n3)
+        ms_r = time_graphs(torch, gr, max(20, args.steps // 2), 5)
+        gp = capture(torch, lambda s: st.enqueue(s, rotated=False), n3)
+        ms_p = time_graphs(torch, gp, max(20, args.steps // 2), 5)
+        res[f"gate_up_decode_M{M}"] = {"GB/s": round(st.bytes() / (ms_r * 1e-3) / 1e9, 2),
+                                       "frac_hbm": round(st.bytes() / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                       "us": round(ms_r * 1e3, 3),
+                                       "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
+        del gr, gp
+    L3.copies = []
+    L4 = Linear(rl, torch, W.make_linear(4, 0))
+    st = Step(rl, torch, [L4], [2048])
+    gr = capture(torch, lambda s: st.enqueue(s), 1)
+    ms_r = time_graphs(torch, gr, 20, 3)
+    gp = capture(torch, lambda s: st.enqueue(s, rotated=False), 1)
+    ms_p = time_graphs(torch, gp, 20, 3)
+    tf = st.flops() / (ms_r * 1e-3) / 1e12
+    res["down_prefill_M2048"] = {"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                 "us": round(ms_r * 1e3, 2),
+                                 "plain_TFLOP/s": round(st.flops() / (ms_p * 1e-3) / 1e12, 2),
+                                 "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
+    return res
+
+
+if __name__ == "__main__":
+    main()

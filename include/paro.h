@@ -89,6 +89,25 @@ int paro_version(void);
 size_t paro_rotation_bytes(int K, int D);
 
 /*
+ * paro_rotation_encode -- host-only half of paro_rotation_prepare: validate a
+ * transform (same arguments and errors as paro_rotation_prepare) and write its
+ * descriptor into the HOST buffer desc_host (desc_bytes >= paro_rotation_bytes).
+ * Makes no HIP call. Copying those bytes to 16-byte aligned device memory and
+ * setting paro_rotation {K, D, device pointer} is equivalent to
+ * paro_rotation_prepare.
+ *
+ * Descriptor layout (each section starts at a multiple of 256 bytes, in order):
+ *   struct { uint32 i | (j << 16); float cos; float sin; } rec[K][D/2]   (12 bytes each)
+ *   float  inv_s[D]        float32(1 / s)
+ *   float  s[D]
+ * Within a stage the pairs are stored in a library-chosen order, and a pair
+ * (i, j, cos, sin) may be stored as (j, i, cos, -sin), which is the same
+ * rotation; the order is a function of the set of pairs only.
+ */
+paro_status paro_rotation_encode(int K, int D, const int32_t* pairs_host, const float* theta_host,
+                                 const float* scale_host, void* desc_host, size_t desc_bytes);
+
+/*
  * paro_rotation_prepare -- validate a transform and upload its descriptor.
  *
  * Defines the transform of section "A rotation small enough to execute":
@@ -97,8 +116,7 @@ size_t paro_rotation_bytes(int K, int D);
  *   theta_host  float32 [K][D/2]: one angle per pair per stage (finite);
  *   scale_host  float32 [D]: channel scales s > 0 (finite).
  * cos/sin are evaluated in float64 by the C library and rounded once to
- * float32; 1/s is rounded once to float32. The descriptor (stage pairs as two
- * uint16, (cos, sin) as float32, 1/s and s as float32) is copied into
+ * float32; 1/s is rounded once to float32. The descriptor (layout above) is copied into
  * desc_dev (desc_bytes >= paro_rotation_bytes(K, D)) on `stream`, which is then
  * synchronized so the host arrays may be released on return. On success *out
  * = {K, D, desc_dev}. Nothing is written to the device on an error.

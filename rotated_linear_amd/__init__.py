@@ -59,6 +59,8 @@ _lib.paro_status_str.argtypes = [_i]
 _lib.paro_version.restype = _i
 _lib.paro_rotation_bytes.restype = _sz
 _lib.paro_rotation_bytes.argtypes = [_i, _i]
+_lib.paro_rotation_encode.restype = _i
+_lib.paro_rotation_encode.argtypes = [_i, _i, _vp, _vp, _vp, _vp, _sz]
 _lib.paro_rotation_prepare.restype = _i
 _lib.paro_rotation_prepare.argtypes = [_i, _i, _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(paro_rotation), _vp]
 _lib.paro_pack_weights.restype = _i
@@ -73,7 +75,7 @@ _lib.paro_rotated_linear.restype = _i
 _lib.paro_rotated_linear.argtypes = [ctypes.POINTER(paro_rotation), _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp,
                                      _sz, _vp]
 
-EXPORTS = ("paro_status_str", "paro_version", "paro_rotation_bytes", "paro_rotation_prepare",
+EXPORTS = ("paro_status_str", "paro_version", "paro_rotation_bytes", "paro_rotation_encode", "paro_rotation_prepare",
            "paro_pack_weights", "paro_rotate", "paro_workspace_bytes", "paro_w4a16_linear",
            "paro_rotated_linear")
 
@@ -141,6 +143,45 @@ def _want(t, dtype, shape, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _host_transform(pairs, theta, scale):
+    pairs = np.ascontiguousarray(np.asarray(pairs, np.int32))
+    theta = np.ascontiguousarray(np.asarray(theta, np.float32))
+    scale = np.ascontiguousarray(np.asarray(scale, np.float32))
+    D = int(scale.shape[0])
+    K = int(pairs.shape[0]) if pairs.ndim == 3 else 0
+    if pairs.ndim != 3 or pairs.shape[1:] != (D // 2, 2) or theta.shape != (K, D // 2):
+        raise ValueError("pairs must be [K][D/2][2] and theta [K][D/2] with D = len(scale)")
+    return pairs, theta, scale, K, D
+
+
+def paro_rotation_encode(pairs, theta, scale) -> np.ndarray:
+    """Host-only: validate the transform and return its descriptor bytes (uint8 array)."""
+    pairs, theta, scale, K, D = _host_transform(pairs, theta, scale)
+    nbytes = _lib.paro_rotation_bytes(K, D)
+    if nbytes == 0:
+        raise ParoError(2, "paro_rotation_bytes")
+    buf = np.zeros(nbytes, np.uint8)
+    _check(_lib.paro_rotation_encode(K, D, pairs.ctypes.data_as(_vp), theta.ctypes.data_as(_vp),
+                                     scale.ctypes.data_as(_vp), buf.ctypes.data_as(_vp), nbytes),
+           "paro_rotation_encode")
+    return buf
+
+
+def descriptor_sections(buf: np.ndarray, K: int, D: int):
+    """Views of an encoded descriptor: pairs (i, j) int [K][D/2][2], cs float32 [K][D/2][2],
+    inv_s float32 [D], s float32 [D]."""
+    def up(v):
+        return (v + 255) // 256 * 256
+    P = K * (D // 2)
+    o_inv = up(P * 12)
+    o_s = o_inv + up(D * 4)
+    rec = buf[:P * 12].view(np.uint32).reshape(K, D // 2, 3)
+    raw = rec[:, :, 0]
+    pairs = np.stack([raw & 0xFFFF, raw >> 16], axis=-1).astype(np.int64)
+    cs = rec[:, :, 1:3].copy().view(np.float32)
+    return pairs, cs, buf[o_inv:o_inv + D * 4].view(np.float32), buf[o_s:o_s + D * 4].view(np.float32)
+
+
 class Rotation:
     """A prepared transform: the device descriptor (a uint8 tensor) and its C handle."""
 
@@ -155,13 +196,7 @@ class Rotation:
 def paro_rotation_prepare(pairs, theta, scale, device="cuda") -> Rotation:
     """pairs int32 [K][D/2][2], theta float32 [K][D/2], scale float32 [D] (host arrays)."""
     torch = _torch()
-    pairs = np.ascontiguousarray(np.asarray(pairs, np.int32))
-    theta = np.ascontiguousarray(np.asarray(theta, np.float32))
-    scale = np.ascontiguousarray(np.asarray(scale, np.float32))
-    D = int(scale.shape[0])
-    K = int(pairs.shape[0]) if pairs.ndim == 3 else 0
-    if pairs.ndim != 3 or pairs.shape[1:] != (D // 2, 2) or theta.shape != (K, D // 2):
-        raise ValueError("pairs must be [K][D/2][2] and theta [K][D/2] with D = len(scale)")
+    pairs, theta, scale, K, D = _host_transform(pairs, theta, scale)
     nbytes = _lib.paro_rotation_bytes(K, D)
     if nbytes == 0:
         raise ParoError(2, "paro_rotation_bytes")

@@ -26,7 +26,7 @@ COMMON = [
 ]
 # per-file extras: the build-time pack must round every float64 product and sum on its own
 EXTRA = {"pack.hip": ["-ffp-contract=off"]}
-SOURCES = ["paro_api.cpp", "pack.hip", "rotate.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["paro_api.cpp", "schedule.cpp", "pack.hip", "rotate.hip", "decode.hip", "gemm.hip"]
 
 
 def _hipcc() -> str:

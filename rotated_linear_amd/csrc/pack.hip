@@ -62,8 +62,7 @@ __device__ inline double f16_bits_to_f64(uint16_t h) {
 }
 
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(int D, int K, const uint16_t* __restrict__ W,
-                                                                  const uint32_t* __restrict__ pairs,
-                                                                  const float2* __restrict__ cs,
+                                                                  const PairRec* __restrict__ recs,
                                                                   const float* __restrict__ s,
                                                                   uint8_t* __restrict__ qweight,
                                                                   uint16_t* __restrict__ scales,
@@ -79,10 +78,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(int D, int K, c
   const int P = D / 2;
   for (int k = 0; k < K; ++k) {
     for (int p = tid; p < P; p += kPackThreads) {
-      const uint32_t ij = pairs[size_t(k) * P + p];
-      const float2 t = cs[size_t(k) * P + p];
-      const int i = int(ij & 0xFFFFu), j = int(ij >> 16);
-      const double c = t.x, sn = t.y;
+      const PairRec r = recs[size_t(k) * P + p];
+      const int i = int(r.ij & 0xFFFFu), j = int(r.ij >> 16);
+      const double c = r.c, sn = r.s;
       const double bi = brow[i], bj = brow[j];
       brow[i] = c * bi + sn * bj;
       brow[j] = c * bj - sn * bi;
@@ -134,7 +132,7 @@ hipError_t launch_pack(const DevRot& R, int N, const uint16_t* W, uint8_t* qweig
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pack_rows_kernel, dim3(N), dim3(kPackThreads), lds, st, R.D, R.K, W, R.pairs, R.cs, R.s,
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(N), dim3(kPackThreads), lds, st, R.D, R.K, W, R.rec, R.s,
                      qweight, scales, zeros);
   return hipGetLastError();
 }

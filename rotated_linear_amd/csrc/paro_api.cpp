@@ -33,8 +33,8 @@ paro_status check_rotation(const paro_rotation* r) {
 
 paro_status from_hip(hipError_t e) { return e == hipSuccess ? PARO_OK : PARO_EHIP; }
 
-size_t linear_ws_bytes(bool rotated, int M, int D) {
-  if (!rotated || M <= 0 || fused_decode_ok(M, D)) return 0;
+size_t linear_ws_bytes(bool rotated, int M, int D, int N) {
+  if (!rotated || M <= 0 || fused_decode_ok(M, D, N)) return 0;
   return align256(size_t(M) * size_t(D) * 2);
 }
 
@@ -57,10 +57,12 @@ paro_status check_linear_args(int M, int D, int N, const void* x, const uint8_t*
 
 }  // namespace
 
-bool paro::fused_decode_ok(int M, int D) {
-  // rotation buffer (float32 [D][M]) + transformed activations (float16 [M][D]) in LDS
-  const int mr = M == 1 ? 1 : (M == 2 ? 2 : 4);  // rows the kernel instance holds
-  return M >= 1 && M <= kFusedMaxM && size_t(mr) * size_t(D) * 6 <= 96u * 1024u;
+bool paro::fused_decode_ok(int M, int D, int N) {
+  return M >= 1 && M <= kFusedMaxM && N >= 1 && decode_lds_bytes(true, M, D, N) <= kDecodeMaxLds;
+}
+
+bool paro::decode_ok(int M, int D, int N) {
+  return M >= 1 && M <= kDecodeMaxM && N >= 1 && decode_lds_bytes(false, M, D, N) <= kDecodeMaxLds;
 }
 
 extern "C" {
@@ -85,22 +87,15 @@ size_t paro_rotation_bytes(int K, int D) {
   return desc_layout(K, D).total;
 }
 
-paro_status paro_rotation_prepare(int K, int D, const int32_t* pairs_host, const float* theta_host,
-                                  const float* scale_host, void* desc_dev, size_t desc_bytes,
-                                  paro_rotation* out, void* stream) {
-  if (!out || !desc_dev || !scale_host || (K > 0 && (!pairs_host || !theta_host))) return PARO_EINVAL;
+paro_status paro_rotation_encode(int K, int D, const int32_t* pairs_host, const float* theta_host,
+                                 const float* scale_host, void* desc_host, size_t desc_bytes) {
+  if (!desc_host || !scale_host || (K > 0 && (!pairs_host || !theta_host))) return PARO_EINVAL;
   if (paro_status s = check_shape(K, D)) return s;
-  if (!aligned16(desc_dev)) return PARO_EINVAL;
   const DescLayout L = desc_layout(K, D);
   if (desc_bytes < L.total) return PARO_EINVAL;
   const int P = D / 2;
 
-  std::vector<unsigned char> host(L.total, 0);
-  uint32_t* pr = reinterpret_cast<uint32_t*>(host.data() + L.pairs_off);
-  float* cs = reinterpret_cast<float*>(host.data() + L.cs_off);
-  float* inv_s = reinterpret_cast<float*>(host.data() + L.inv_s_off);
-  float* s = reinterpret_cast<float*>(host.data() + L.s_off);
-
+  // validate everything before writing anything
   std::vector<int> seen(D);
   for (int k = 0; k < K; ++k) {
     std::fill(seen.begin(), seen.end(), 0);
@@ -109,20 +104,56 @@ paro_status paro_rotation_prepare(int K, int D, const int32_t* pairs_host, const
       const int32_t j = pairs_host[(size_t(k) * P + p) * 2 + 1];
       if (i < 0 || i >= D || j < 0 || j >= D || i == j || seen[i] || seen[j]) return PARO_EPAIRS;
       seen[i] = seen[j] = 1;
-      const float t = theta_host[size_t(k) * P + p];
-      if (!isfinite(t)) return PARO_ESCALE;
-      pr[size_t(k) * P + p] = uint32_t(i) | (uint32_t(j) << 16);
-      cs[(size_t(k) * P + p) * 2 + 0] = static_cast<float>(cos(static_cast<double>(t)));
-      cs[(size_t(k) * P + p) * 2 + 1] = static_cast<float>(sin(static_cast<double>(t)));
+      if (!isfinite(theta_host[size_t(k) * P + p])) return PARO_ESCALE;
     }
   }
   for (int c = 0; c < D; ++c) {
     const float v = scale_host[c];
     if (!isfinite(v) || !(v > 0.0f)) return PARO_ESCALE;
-    s[c] = v;
-    inv_s[c] = static_cast<float>(1.0 / static_cast<double>(v));
-    if (!isfinite(inv_s[c]) || inv_s[c] == 0.0f) return PARO_ESCALE;
+    const float inv = static_cast<float>(1.0 / static_cast<double>(v));
+    if (!isfinite(inv) || inv == 0.0f) return PARO_ESCALE;
   }
+
+  unsigned char* base = static_cast<unsigned char*>(desc_host);
+  memset(base, 0, L.total);
+  PairRec* rec = reinterpret_cast<PairRec*>(base + L.rec_off);
+  float* inv_s = reinterpret_cast<float*>(base + L.inv_s_off);
+  float* s = reinterpret_cast<float*>(base + L.s_off);
+  std::vector<StagePair> stage(P);
+  for (int k = 0; k < K; ++k) {
+    for (int p = 0; p < P; ++p) {
+      const float t = theta_host[size_t(k) * P + p];
+      stage[p].i = pairs_host[(size_t(k) * P + p) * 2 + 0];
+      stage[p].j = pairs_host[(size_t(k) * P + p) * 2 + 1];
+      stage[p].c = static_cast<float>(cos(static_cast<double>(t)));
+      stage[p].s = static_cast<float>(sin(static_cast<double>(t)));
+    }
+    if (!schedule_stage(D, stage)) return PARO_EPAIRS;
+    for (int p = 0; p < P; ++p) {
+      PairRec& r = rec[size_t(k) * P + p];
+      r.ij = uint32_t(stage[p].i) | (uint32_t(stage[p].j) << 16);
+      r.c = stage[p].c;
+      r.s = stage[p].s;
+    }
+  }
+  for (int c = 0; c < D; ++c) {
+    s[c] = scale_host[c];
+    inv_s[c] = static_cast<float>(1.0 / static_cast<double>(scale_host[c]));
+  }
+  return PARO_OK;
+}
+
+paro_status paro_rotation_prepare(int K, int D, const int32_t* pairs_host, const float* theta_host,
+                                  const float* scale_host, void* desc_dev, size_t desc_bytes,
+                                  paro_rotation* out, void* stream) {
+  if (!out || !desc_dev) return PARO_EINVAL;
+  if (paro_status s = check_shape(K, D)) return s;
+  if (!aligned16(desc_dev)) return PARO_EINVAL;
+  const DescLayout L = desc_layout(K, D);
+  if (desc_bytes < L.total) return PARO_EINVAL;
+  std::vector<unsigned char> host(L.total);
+  if (paro_status s = paro_rotation_encode(K, D, pairs_host, theta_host, scale_host, host.data(), host.size()))
+    return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(desc_dev, host.data(), L.total, hipMemcpyHostToDevice, st) != hipSuccess) return PARO_EHIP;
   if (hipStreamSynchronize(st) != hipSuccess) return PARO_EHIP;
@@ -158,18 +189,18 @@ paro_status paro_rotate(const paro_rotation* r, int M, const void* x, void* xout
   const size_t bytes = size_t(M) * size_t(r->D) * 2;
   if (overlap(x, bytes, xout, bytes)) return PARO_EINVAL;
   return from_hip(launch_rotate(dev_rot(*r), M, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xout),
-                                static_cast<hipStream_t>(stream)));
+                                false, static_cast<hipStream_t>(stream)));
 }
 
 size_t paro_workspace_bytes(int M, int D, int N) {
-  (void)N;
-  if (M <= 0 || check_shape(0, D) != PARO_OK) return 0;
-  return linear_ws_bytes(true, M, D);
+  if (M <= 0 || N < 0 || check_shape(0, D) != PARO_OK) return 0;
+  return linear_ws_bytes(true, M, D, N);
 }
 
-static paro_status run_linear(int M, int D, int N, const uint16_t* x, const uint8_t* qweight,
+static paro_status run_linear(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
                               const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, hipStream_t st) {
-  if (M <= kGemvMaxM) return from_hip(launch_gemv(nullptr, M, D, N, x, qweight, scales, zeros, y, ydtype, st));
+  if (decode_ok(M, D, N))
+    return from_hip(launch_decode(nullptr, M, D, N, x, x_nibble_order, qweight, scales, zeros, y, ydtype, st));
   return from_hip(launch_gemm(M, D, N, x, qweight, scales, zeros, y, ydtype, st));
 }
 
@@ -180,7 +211,7 @@ paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t*
   if (paro_status s = check_shape(0, D)) return s;
   if (paro_status s = check_linear_args(M, D, N, x, qweight, scales, zeros, y, ydtype)) return s;
   if (M == 0 || N == 0) return PARO_OK;
-  return run_linear(M, D, N, static_cast<const uint16_t*>(x), qweight, static_cast<const uint16_t*>(scales),
+  return run_linear(M, D, N, static_cast<const uint16_t*>(x), false, qweight, static_cast<const uint16_t*>(scales),
                     static_cast<const uint16_t*>(zeros), y, ydtype, static_cast<hipStream_t>(stream));
 }
 
@@ -193,19 +224,20 @@ paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void
   if (M == 0 || N == 0) return PARO_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const DevRot R = dev_rot(*r);
-  if (fused_decode_ok(M, D))
-    return from_hip(launch_gemv(&R, M, D, N, static_cast<const uint16_t*>(x), qweight,
-                                static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), y,
-                                ydtype, st));
-  const size_t need = linear_ws_bytes(true, M, D);
+  if (fused_decode_ok(M, D, N))
+    return from_hip(launch_decode(&R, M, D, N, static_cast<const uint16_t*>(x), false, qweight,
+                                  static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), y,
+                                  ydtype, st));
+  const size_t need = linear_ws_bytes(true, M, D, N);
   if (!ws || ws_bytes < need) return PARO_EWORKSPACE;
   if (!aligned16(ws)) return PARO_EINVAL;
   const size_t ybytes = size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2);
   if (overlap(ws, need, x, size_t(M) * D * 2) || overlap(ws, need, y, ybytes)) return PARO_EINVAL;
   uint16_t* xr = static_cast<uint16_t*>(ws);
-  if (hipError_t e = launch_rotate(R, M, static_cast<const uint16_t*>(x), xr, st)) return from_hip(e);
-  return run_linear(M, D, N, xr, qweight, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
-                    y, ydtype, st);
+  const bool nib = decode_ok(M, D, N);  // the decode kernel takes its A operand in nibble order
+  if (hipError_t e = launch_rotate(R, M, static_cast<const uint16_t*>(x), xr, nib, st)) return from_hip(e);
+  return run_linear(M, D, N, xr, nib, qweight, static_cast<const uint16_t*>(scales),
+                    static_cast<const uint16_t*>(zeros), y, ydtype, st);
 }
 
 }  // extern "C"

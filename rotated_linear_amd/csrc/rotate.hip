@@ -2,134 +2,123 @@
 // then division by the channel scales ("ParoQuant: pairwise rotations that
 // survive deployment", section "A rotation small enough to execute").
 //
-// One workgroup transforms R rows. The rows live in LDS as float32 for all K
-// stages, interleaved by channel (lds[c][r]), so one LDS access moves a pair's
-// element for all R rows. Each thread owns pairs p = tid, tid + NT, ...; the
-// pairs of a stage touch disjoint channels, so a stage is one pass with no
-// write conflicts and one barrier. The pair list and (cos, sin) of stage k+1
-// are fetched into registers while stage k computes. 1/s is applied on the
-// way out, with one float32 -> float16 rounding.
-#include "paro_internal.h"
+// One workgroup of 512 threads transforms R rows held in LDS as float32 for all
+// K stages (rotation_core.h). Stage parameters stream through a register ring
+// issued before the rows are even loaded; 1/s is applied on the way out with one
+// float32 -> float16 rounding. With PERM the output keeps every 8-channel word in
+// the order the INT4 decode of the linear kernels produces ([0,4,1,5,2,6,3,7]),
+// which is how paro_rotated_linear hands its workspace to them.
+#include "rotation_core.h"
 
 namespace paro {
 namespace {
 
-template <int R>
-struct RowVec {
-  using T = float __attribute__((ext_vector_type(R)));
-};
-template <>
-struct RowVec<1> {
-  using T = float;
-};
-
 constexpr int kRotThreads = 512;
-constexpr int kMaxPairsPerThread = PARO_MAX_D / 2 / kRotThreads;  // 16
 
-template <int R>
+template <int R, int PPT, int PD, bool EXACT, bool PERM>
 __global__ __launch_bounds__(kRotThreads) void rotate_rows_kernel(const uint16_t* __restrict__ x,
                                                                    uint16_t* __restrict__ xout, int M, int D,
-                                                                   int K, const uint32_t* __restrict__ pairs,
-                                                                   const float2* __restrict__ cs,
+                                                                   int K, const PairRec* __restrict__ recs,
                                                                    const float* __restrict__ inv_s) {
-  using V = typename RowVec<R>::T;
-  extern __shared__ float lds[];  // [D][R]
-  V* rows = reinterpret_cast<V*>(lds);
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [D][R]
   const int tid = threadIdx.x;
   const int row0 = blockIdx.x * R;
-  const int chunks = D / 8;  // 8 halves = 16 bytes per global access
-
-  for (int e = tid; e < chunks * R; e += kRotThreads) {
-    const int r = e / chunks, c8 = e - r * chunks;
-    const int row = row0 + r;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < M) v = *reinterpret_cast<const uint4*>(x + size_t(row) * D + c8 * 8);
-    const _Float16* h = reinterpret_cast<const _Float16*>(&v);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) lds[(c8 * 8 + t) * R + r] = static_cast<float>(h[t]);
-  }
-
   const int P = D / 2;
-  const int npp = (P - tid + kRotThreads - 1) / kRotThreads;  // pairs this thread owns per stage
-  uint32_t ij[kMaxPairsPerThread];
-  float2 t[kMaxPairsPerThread];
-  if (K > 0) {
-#pragma unroll
-    for (int q = 0; q < kMaxPairsPerThread; ++q)
-      if (q < npp) {
-        ij[q] = pairs[tid + q * kRotThreads];
-        t[q] = cs[tid + q * kRotThreads];
-      }
-  }
-  __syncthreads();
+  const int words = D / 8;  // 16-byte words per row
+  const int total = words * R;
 
-  for (int k = 0; k < K; ++k) {
-    uint32_t nij[kMaxPairsPerThread];
-    float2 nt[kMaxPairsPerThread];
-    const bool more = k + 1 < K;
+  StageRing<kRotThreads, PPT, PD, EXACT> ring;
+  if (K > 0) ring_prime(ring, K, P, tid, recs);
+
+  // rows -> LDS, four 16-byte loads in flight per thread per batch
+  for (int base = 0; base < total; base += 4 * kRotThreads) {
+    uint4 v[4];
 #pragma unroll
-    for (int q = 0; q < kMaxPairsPerThread; ++q)
-      if (more && q < npp) {
-        nij[q] = pairs[size_t(k + 1) * P + tid + q * kRotThreads];
-        nt[q] = cs[size_t(k + 1) * P + tid + q * kRotThreads];
+    for (int u = 0; u < 4; ++u) {
+      int e = base + tid + u * kRotThreads;
+      e = e < total ? e : total - 1;
+      const int r = e / words, w = e - r * words;
+      int row = row0 + r;
+      row = row < M ? row : M - 1;
+      v[u] = *reinterpret_cast<const uint4*>(x + size_t(row) * D + size_t(w) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = base + tid + u * kRotThreads;
+      if (e < total) {
+        const int r = e / words, w = e - r * words;
+        const _Float16* h = reinterpret_cast<const _Float16*>(&v[u]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) lds[(w * 8 + t) * R + r] = static_cast<float>(h[t]);
       }
-#pragma unroll
-    for (int q = 0; q < kMaxPairsPerThread; ++q)
-      if (q < npp) {
-        const int i = int(ij[q] & 0xFFFFu), j = int(ij[q] >> 16);
-        const float c = t[q].x, s = t[q].y;
-        const V vi = rows[i], vj = rows[j];
-        rows[i] = c * vi + s * vj;
-        rows[j] = c * vj - s * vi;
-      }
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int q = 0; q < kMaxPairsPerThread; ++q)
-        if (q < npp) {
-          ij[q] = nij[q];
-          t[q] = nt[q];
-        }
     }
   }
+  __syncthreads();
+  if (K > 0) ring_run<R>(ring, lds, K, P, tid, recs);
 
-  for (int e = tid; e < chunks * R; e += kRotThreads) {
-    const int r = e / chunks, c8 = e - r * chunks;
+  for (int e = tid; e < total; e += kRotThreads) {
+    const int r = e / words, w = e - r * words;
     const int row = row0 + r;
     if (row >= M) continue;
     _Float16 h[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int c = c8 * 8 + u;
-      h[u] = static_cast<_Float16>(lds[c * R + r] * inv_s[c]);
+      const int c = w * 8 + u;
+      h[PERM ? nib_slot(u) : u] = static_cast<_Float16>(lds[c * R + r] * inv_s[c]);
     }
-    *reinterpret_cast<uint4*>(xout + size_t(row) * D + c8 * 8) = *reinterpret_cast<const uint4*>(h);
+    *reinterpret_cast<uint4*>(xout + size_t(row) * D + size_t(w) * 8) = *reinterpret_cast<const uint4*>(h);
   }
 }
 
-template <int R>
+template <int R, int PPT, int PD, bool EXACT, bool PERM>
 hipError_t launch_rows(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
   const size_t lds = size_t(Rt.D) * R * sizeof(float);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rotate_rows_kernel<R>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rotate_rows_kernel<R, PPT, PD, EXACT, PERM>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
   const int blocks = (M + R - 1) / R;
-  hipLaunchKernelGGL(rotate_rows_kernel<R>, dim3(blocks), dim3(kRotThreads), lds, st, x, xout, M, Rt.D, Rt.K,
-                     Rt.pairs, Rt.cs, Rt.inv_s);
+  hipLaunchKernelGGL((rotate_rows_kernel<R, PPT, PD, EXACT, PERM>), dim3(blocks), dim3(kRotThreads), lds, st, x,
+                     xout, M, Rt.D, Rt.K, Rt.rec, Rt.inv_s);
   return hipGetLastError();
+}
+
+template <int R, int PPT, int PD, bool PERM>
+hipError_t launch_exact(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
+  if (Rt.D / 2 == PPT * kRotThreads) return launch_rows<R, PPT, PD, true, PERM>(Rt, M, x, xout, st);
+  return launch_rows<R, PPT, PD, false, PERM>(Rt, M, x, xout, st);
+}
+
+template <int R, bool PERM>
+hipError_t launch_ppt(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
+  const int ppt = (Rt.D / 2 + kRotThreads - 1) / kRotThreads;  // pairs per thread per stage
+  if (ppt <= 1) return launch_exact<R, 1, 8, PERM>(Rt, M, x, xout, st);
+  if (ppt <= 2) return launch_exact<R, 2, 8, PERM>(Rt, M, x, xout, st);
+  if (ppt <= 3) return launch_exact<R, 3, 8, PERM>(Rt, M, x, xout, st);
+  if (ppt <= 4) return launch_exact<R, 4, 4, PERM>(Rt, M, x, xout, st);
+  if (ppt <= 6) return launch_exact<R, 6, 4, PERM>(Rt, M, x, xout, st);
+  if (ppt <= 9) return launch_exact<R, 9, 2, PERM>(Rt, M, x, xout, st);
+  if (ppt <= 12) return launch_exact<R, 12, 2, PERM>(Rt, M, x, xout, st);
+  return launch_exact<R, 16, 2, PERM>(Rt, M, x, xout, st);
+}
+
+template <bool PERM>
+hipError_t launch_r(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
+  // Rows per workgroup: amortize the stage parameters over several rows once there are
+  // enough rows to keep >= 512 workgroups, within 80 KB of LDS (two workgroups per CU).
+  const size_t row_bytes = size_t(R.D) * 4;
+  if (M >= 4 * 512 && 4 * row_bytes <= 80 * 1024) return launch_ppt<4, PERM>(R, M, x, xout, st);
+  if (M >= 2 * 512 && 2 * row_bytes <= 80 * 1024) return launch_ppt<2, PERM>(R, M, x, xout, st);
+  return launch_ppt<1, PERM>(R, M, x, xout, st);
 }
 
 }  // namespace
 
-hipError_t launch_rotate(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  // Rows per workgroup: as many as keep the LDS image within 80 KB (two workgroups per CU),
-  // but no more than the batch has.
-  const size_t row_bytes = size_t(R.D) * 4;
-  if (M >= 4 && 4 * row_bytes <= 80 * 1024) return launch_rows<4>(R, M, x, xout, st);
-  if (M >= 2 && 2 * row_bytes <= 80 * 1024) return launch_rows<2>(R, M, x, xout, st);
-  return launch_rows<1>(R, M, x, xout, st);
+hipError_t launch_rotate(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, bool nibble_order,
+                         hipStream_t st) {
+  if (R.D / 2 > 16 * kRotThreads) return hipErrorInvalidValue;
+  return nibble_order ? launch_r<true>(R, M, x, xout, st) : launch_r<false>(R, M, x, xout, st);
 }
 
 }  // namespace paro

@@ -1,0 +1,135 @@
+// Device-side Givens stages over activation rows held in LDS, shared by the
+// standalone transform kernel and the fused decode kernel.
+//
+// Layout: R rows interleaved by channel, lds[c * R + r] (float32), so one LDS
+// access moves channel c of all R rows. Stage k updates, for each of its pairs
+// (i, j, c, s):  x_i <- c x_i + s x_j,  x_j <- c x_j - s x_i  ("ParoQuant:
+// pairwise rotations that survive deployment", section "A rotation small enough
+// to execute"). Thread t owns pairs t, t + NT, ... of every stage; the host
+// orders each stage so a wave's gathers spread over the LDS banks.
+//
+// Each pair is one 12-byte record {i | j << 16, cos, sin}: one 3-dword load.
+// The records of PD stages are kept in flight in a register ring: loading
+// stage k + PD is issued right after stage k. Loads are branch-free (indices
+// clamped into range) and the stage sequence is straight-line code for K <= 8,
+// so the compiler's wait counts stay exact and a stage waits only for its own
+// records. With EXACT (the stage's pairs divide evenly over the threads) the
+// per-pair range checks disappear as well.
+#pragma once
+
+#include "paro_internal.h"
+
+namespace paro {
+
+// Stage counts up to this run as straight-line code (the common K = 8 of the method).
+constexpr int kUnrolledStages = 8;
+
+template <int R>
+struct RowVec {
+  using T = float __attribute__((ext_vector_type(R)));
+};
+template <>
+struct RowVec<1> {
+  using T = float;
+};
+
+template <int NT, int PPT, int PD, bool EXACT>
+struct StageRing {
+  PairRec rec[PD][PPT];
+
+  // Issue the loads of stage k (clamped into [0, K)) into ring slot `slot`.
+  template <int slot>
+  __device__ inline void issue(int k, int K, int P, int tid, const PairRec* __restrict__ recs) {
+    const int kc = k < K ? k : K - 1;
+    const size_t base = size_t(kc) * size_t(P);
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      int p = tid + q * NT;
+      if constexpr (!EXACT) p = p < P ? p : P - 1;
+      rec[slot][q] = recs[base + p];
+    }
+  }
+
+  // All of the thread's gathers first, then all updates: the pairs of a stage are disjoint,
+  // but the compiler cannot know that, so interleaving reads and writes per pair would
+  // serialize every pair behind the previous pair's LDS round trip.
+  template <int R, int slot>
+  __device__ inline void apply(typename RowVec<R>::T* rows, int P, int tid) const {
+    using V = typename RowVec<R>::T;
+    V vi[PPT], vj[PPT];
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      if (EXACT || tid + q * NT < P) {
+        vi[q] = rows[rec[slot][q].ij & 0xFFFFu];
+        vj[q] = rows[rec[slot][q].ij >> 16];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      if (EXACT || tid + q * NT < P) {
+        const float c = rec[slot][q].c, s = rec[slot][q].s;
+        rows[rec[slot][q].ij & 0xFFFFu] = c * vi[q] + s * vj[q];
+        rows[rec[slot][q].ij >> 16] = c * vj[q] - s * vi[q];
+      }
+    }
+  }
+};
+
+template <int NT, int PPT, int PD, bool EXACT, int slot = 0>
+__device__ inline void ring_prime(StageRing<NT, PPT, PD, EXACT>& ring, int K, int P, int tid,
+                                  const PairRec* __restrict__ recs) {
+  if constexpr (slot < PD) {
+    ring.template issue<slot>(slot, K, P, tid, recs);
+    ring_prime<NT, PPT, PD, EXACT, slot + 1>(ring, K, P, tid, recs);
+  }
+}
+
+template <int R, int NT, int PPT, int PD, bool EXACT, int slot = 0>
+__device__ inline void ring_round(StageRing<NT, PPT, PD, EXACT>& ring, typename RowVec<R>::T* rows, int k0, int K,
+                                  int P, int tid, const PairRec* __restrict__ recs) {
+  if constexpr (slot < PD) {
+    const int k = k0 + slot;
+    if (k < K) {
+      ring.template apply<R, slot>(rows, P, tid);
+      __syncthreads();
+      ring.template issue<slot>(k + PD, K, P, tid, recs);
+      ring_round<R, NT, PPT, PD, EXACT, slot + 1>(ring, rows, k0, K, P, tid, recs);
+    }
+  }
+}
+
+// Straight-line version for K <= KMAX stages: with no loop back-edge the compiler's wait
+// counts stay exact, so a stage waits only for its own records.
+template <int KMAX, int R, int NT, int PPT, int PD, bool EXACT, int k = 0>
+__device__ inline void ring_unrolled(StageRing<NT, PPT, PD, EXACT>& ring, typename RowVec<R>::T* rows, int K, int P,
+                                     int tid, const PairRec* __restrict__ recs) {
+  if constexpr (k < KMAX) {
+    if (k < K) {  // uniform; holds no global load
+      ring.template apply<R, k % PD>(rows, P, tid);
+      __syncthreads();
+    }
+    if constexpr (k + PD < KMAX) ring.template issue<k % PD>(k + PD, K, P, tid, recs);
+    ring_unrolled<KMAX, R, NT, PPT, PD, EXACT, k + 1>(ring, rows, K, P, tid, recs);
+  }
+}
+
+// Run all K stages (K >= 1) on the rows in LDS. The caller has issued ring_prime() early
+// (ideally before filling LDS) and must __syncthreads() between filling the rows and
+// calling this. Ends with a barrier after the last stage.
+template <int R, int NT, int PPT, int PD, bool EXACT>
+__device__ inline void ring_run(StageRing<NT, PPT, PD, EXACT>& ring, float* lds, int K, int P, int tid,
+                                const PairRec* __restrict__ recs) {
+  using V = typename RowVec<R>::T;
+  V* rows = reinterpret_cast<V*>(lds);
+  if (K <= kUnrolledStages) {
+    ring_unrolled<kUnrolledStages, R, NT, PPT, PD, EXACT>(ring, rows, K, P, tid, recs);
+  } else {
+    for (int k0 = 0; k0 < K; k0 += PD) ring_round<R, NT, PPT, PD, EXACT>(ring, rows, k0, K, P, tid, recs);
+  }
+}
+
+// Slot of channel offset e (0..7) of an 8-channel word in the order the INT4
+// decode produces: [0, 4, 1, 5, 2, 6, 3, 7].
+__device__ inline int nib_slot(int e) { return ((e & 3) << 1) | (e >> 2); }
+
+}  // namespace paro

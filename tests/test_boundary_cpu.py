@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     out = subprocess.run(["nm", "-D", "--defined-only", rl.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(paro_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -44,9 +44,9 @@ def test_status_strings_and_sizes():
         assert lib.paro_status_str(s).decode().startswith(rl.STATUS[s])
     assert lib.paro_status_str(99) == b"PARO_UNKNOWN"
     assert lib.paro_version() >= 100
-    # descriptor: pairs (4 B) + cos/sin (8 B) per pair per stage + 1/s and s (4 B each) per channel,
-    # each section padded to 256 bytes
-    assert rl.paro_rotation_bytes(8, 1536) == 8 * 768 * 4 + 8 * 768 * 8 + 2 * 1536 * 4
+    # descriptor: one 12-byte record (pair word, cos, sin) per pair per stage + 1/s and s (4 B each)
+    # per channel, each section padded to 256 bytes
+    assert rl.paro_rotation_bytes(8, 1536) == 8 * 768 * 12 + 2 * 1536 * 4
     assert rl.paro_rotation_bytes(0, 128) == 2 * 512
     for K, D in ((8, 100), (8, 1537), (-1, 256), (65, 256), (2, 16512), (2, 0)):
         assert rl.paro_rotation_bytes(K, D) == 0, (K, D)
@@ -151,3 +151,66 @@ def test_calls_reject_bad_arguments_before_launch():
     assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, None, 0, None) == 5
     assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, v(FAKE * 6), 100, None) == 5
     assert lib.paro_rotated_linear(None, 1, 512, *args, v(FAKE * 5), 0, None, 0, None) == 1
+
+
+# --------------------------------------------------------------------------- #
+# descriptor encoding and the bank-conflict-free pair order (host only)
+# --------------------------------------------------------------------------- #
+
+def _encode(pairs, theta, scale):
+    K, D = pairs.shape[0], scale.shape[0]
+    return rl.descriptor_sections(rl.paro_rotation_encode(pairs, theta, scale), K, D)
+
+
+@pytest.mark.parametrize("D,K", [(128, 1), (256, 2), (1536, 8), (8960, 2), (16384, 1)])
+def test_schedule_is_conflict_free_and_same_rotation(D, K):
+    import math
+    pairs, theta, scale = _good(K, D, seed=D)
+    ep, ecs, inv_s, s = _encode(pairs, theta, scale)
+    assert np.array_equal(s, scale)
+    assert np.array_equal(inv_s, (1.0 / scale.astype(np.float64)).astype(np.float32))
+    for k in range(K):
+        # same set of rotations: (i, j, c, s) or (j, i, c, -s)
+        want = {}
+        for (i, j), t in zip(pairs[k], theta[k]):
+            c = np.float32(math.cos(float(t)))
+            sn = np.float32(math.sin(float(t)))
+            want[(int(i), int(j))] = (c, sn)
+        for (i, j), (c, sn) in zip(ep[k], ecs[k]):
+            if (int(i), int(j)) in want:
+                assert want[(int(i), int(j))] == (c, sn)
+            else:
+                wc, ws = want[(int(j), int(i))]
+                assert wc == c and ws == -sn
+        assert len(want) == D // 2
+        # every aligned run of q pairs has distinct first and second channels mod q
+        for q in (64, 32, 16, 8):
+            ii = (ep[k, :, 0] % q).reshape(-1, q)
+            jj = (ep[k, :, 1] % q).reshape(-1, q)
+            assert all(len(set(r)) == q for r in ii), (q, "first channels collide")
+            assert all(len(set(r)) == q for r in jj), (q, "second channels collide")
+
+
+def test_schedule_depends_only_on_the_pair_set():
+    pairs, theta, scale = _good(3, 1024, seed=4)
+    base = rl.paro_rotation_encode(pairs, theta, scale)
+    rng = np.random.default_rng(1)
+    p2, t2 = pairs.copy(), theta.copy()
+    for k in range(3):
+        perm = rng.permutation(512)
+        p2[k], t2[k] = p2[k][perm], t2[k][perm]
+    assert np.array_equal(rl.paro_rotation_encode(p2, t2, scale), base)
+
+
+def test_encode_errors_match_prepare():
+    pairs, theta, scale = _good()
+    bad = pairs.copy()
+    bad[0, 1] = bad[0, 0]
+    with pytest.raises(rl.ParoError) as e:
+        rl.paro_rotation_encode(bad, theta, scale)
+    assert e.value.status == 3
+    s = scale.copy()
+    s[3] = -2
+    with pytest.raises(rl.ParoError) as e:
+        rl.paro_rotation_encode(pairs, theta, s)
+    assert e.value.status == 4
