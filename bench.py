@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip the gate+up / down_proj extras")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--traffic", action="store_true",
+                   help="for rocprofv3 --pmc runs: a 256 MiB float16 negation (the counter calibration copy) "
+                        "and then the dominant call over the cold pool, eagerly; prints nothing else")
     return p.parse_args()
 
 
@@ -200,6 +203,9 @@ def main():
     import workloads as W
 
     torch.cuda.init()
+    if args.traffic:
+        traffic_run(rl, torch, W, args.steps)
+        return
     wl = W.WORKLOADS[2]
     linears = [Linear(rl, torch, W.make_linear(2, i)) for i in range(len(wl.linears))]
     Ms = list(wl.Ms)
@@ -230,7 +236,7 @@ def main():
     dom_bytes = workload_bytes(1, 1536, 1536, 8)
     dom_gbs = dom_bytes / (ms_dom * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "decode_kernel<FUSED=1,MR=1> (q proj, M=1, D=1536, N=1536)",
                 "avg_launch_us": round(ms_dom * 1e3, 3), "algorithmic_bytes_per_launch": dom_bytes}
 
@@ -253,6 +259,59 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+CALIB_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_q1536_M1_fused_traffic.md")
+KERNEL_SOURCES = ["rotated_linear_amd/csrc/decode.hip", "rotated_linear_amd/csrc/rotation_core.h",
+                  "rotated_linear_amd/csrc/paro_internal.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
+    when that summary was taken on other kernel sources than the ones built here."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if " = " in line:
+                    k, v = line.split(" = ", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256_16") != kernel_source_hash():
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def dominant_call(rl, torch, W):
+    """The q projection at M=1 (fused transform + decode) with its cold pool."""
+    lin = Linear(rl, torch, W.make_linear(2, 0))
+    lin.make_copies(rl, max(4, math.ceil(POOL_BYTES / lin.set_bytes())))
+    return Step(rl, torch, [lin], [1])
+
+
+def traffic_run(rl, torch, W, reps):
+    a = torch.ones(CALIB_BYTES // 2, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    st = dominant_call(rl, torch, W)
+    for r in range(reps):
+        st.enqueue(r, rotated=True)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_run": {"calls": reps, "calib_bytes": CALIB_BYTES}}), flush=True)
 
 
 def extras(rl, torch, W, args):
