@@ -93,6 +93,9 @@ class Step:
             self.y[(li, M)] = torch.empty((M, lin.N), dtype=torch.float16, device="cuda")
             need = rl.paro_workspace_bytes(M, lin.D, lin.N)
             self.ws[(li, M)] = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        # every call's workspace at once is enough for any batch of these calls
+        self.batch_ws = torch.empty(max(sum(t.numel() for t in self.ws.values()), 256), dtype=torch.uint8,
+                                    device="cuda")
 
     def bytes(self, rotated=True):
         return sum(workload_bytes(M, self.linears[li].D, self.linears[li].N, self.linears[li].K, rotated)
@@ -101,14 +104,30 @@ class Step:
     def flops(self):
         return sum(2.0 * M * self.linears[li].D * self.linears[li].N for li, M in self.calls)
 
-    def enqueue(self, slot, rotated=True, only=None):
+    def _weights(self, li, M, slot):
+        lin = self.linears[li]
+        if lin.copies:
+            return lin.copies[(slot * len(self.Ms) + self.Ms.index(M)) % len(lin.copies)]
+        return lin.rot, lin.w
+
+    def enqueue(self, slot, rotated=True, only=None, batched=False):
+        """Enqueue the step's calls on the current stream: one library call each, or all of them
+        as one paro_linear_batch call (batched)."""
         rl = self.rl
+        if batched:
+            calls, outs = [], []
+            for ci, (li, M) in enumerate(self.calls):
+                if only is not None and ci not in only:
+                    continue
+                rot, w = self._weights(li, M, slot)
+                calls.append((rot if rotated else None, self.x[(li, M)], *w))
+                outs.append(self.y[(li, M)])
+            rl.paro_linear_batch(calls, outs=outs, ws=self.batch_ws)
+            return
         for ci, (li, M) in enumerate(self.calls):
             if only is not None and ci not in only:
                 continue
-            lin = self.linears[li]
-            rot, w = lin.copies[(slot * len(self.Ms) + self.Ms.index(M)) % len(lin.copies)] if lin.copies \
-                else (lin.rot, lin.w)
+            rot, w = self._weights(li, M, slot)
             if rotated:
                 rl.paro_rotated_linear(rot, self.x[(li, M)], *w, out=self.y[(li, M)], ws=self.ws[(li, M)])
             else:

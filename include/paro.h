@@ -34,6 +34,9 @@
  *   - Every pointer argument named *_dev, x, y, W, qweight, scales, zeros, ws
  *     is a DEVICE pointer on the current HIP device; *_host arguments are host
  *     pointers. Device pointers must be 16-byte aligned.
+ *   - The linears read scales and zeros as aligned 32-bit words: when
+ *     N * D/128 is odd, the word holding the last element also covers the 2
+ *     bytes after the array (never a separate page); they are not used.
  *   - The caller owns every buffer. The library allocates nothing, frees
  *     nothing and keeps no mutable global state; calls are re-entrant.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
@@ -149,8 +152,10 @@ paro_status paro_pack_weights(const paro_rotation* r, int N, const void* W, uint
  */
 paro_status paro_rotate(const paro_rotation* r, int M, const void* x, void* xout, void* stream);
 
-/* Workspace bytes paro_w4a16_linear / paro_rotated_linear need for (M, D, N);
- * may be 0. A larger workspace is always accepted. */
+/* Workspace bytes that suffice for paro_w4a16_linear / paro_rotated_linear at
+ * (M, D, N) with any transform: M * D * 2 rounded up to 256 (0 for M <= 0 or an
+ * invalid D). Calls whose transform runs inside the decode kernel (M <= 16,
+ * D <= 4096, K <= 8) and plain linears use none of it and accept ws == NULL. */
 size_t paro_workspace_bytes(int M, int D, int N);
 
 /*
@@ -170,13 +175,47 @@ paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t*
  * paro_rotated_linear -- the fused runtime path: the activation transform of
  * paro_rotate (float32, rounded once to float16 as the linear's 16-bit
  * operand) immediately followed by the INT4 linear of paro_w4a16_linear, with
- * the weights packed by paro_pack_weights for the same transform. Small M runs
- * as one kernel; large M as a transform kernel writing into ws followed by the
- * MFMA GEMM, on `stream`. Arguments as in paro_w4a16_linear, with D = r->D.
+ * the weights packed by paro_pack_weights for the same transform. With M <= 16,
+ * D <= 4096 and K <= 8 the transform runs inside the decode kernel (one launch,
+ * no workspace); otherwise a transform kernel writes x' into ws (at least
+ * M * D * 2 bytes, else PARO_EWORKSPACE) and the linear reads it, on `stream`.
+ * Arguments as in paro_w4a16_linear, with D = r->D.
  */
 paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void* x,
                                 const uint8_t* qweight, const void* scales, const void* zeros,
                                 void* y, int ydtype, void* ws, size_t ws_bytes, void* stream);
+
+/* One linear of a batch: paro_rotated_linear(rot, ...) when rot != NULL (then D
+ * must equal rot->D), else paro_w4a16_linear(M, D, N, ...). Pointers as there. */
+typedef struct {
+  const paro_rotation* rot;
+  int32_t M;
+  int32_t D;
+  int32_t N;
+  const void* x;
+  const uint8_t* qweight;
+  const void* scales;
+  const void* zeros;
+  void* y;
+} paro_linear_args;
+
+/* Workspace bytes paro_linear_batch needs for these calls (may be 0). */
+size_t paro_linear_batch_workspace_bytes(int count, const paro_linear_args* calls);
+
+/*
+ * paro_linear_batch -- `count` independent linears of the kind above (a decode
+ * step's projections, say), each computing bit for bit what its single call
+ * computes. The decode-shaped calls
+ * (M <= 16) that share D run as one launch of the decode kernel, their
+ * transforms inside it where the single call would; the others run one after
+ * the other, using consecutive slices of ws (ws_bytes >=
+ * paro_linear_batch_workspace_bytes). The calls may run concurrently, so no
+ * call's y may overlap any buffer of another call (PARO_EINVAL); every call is
+ * checked as its single call would be before anything is enqueued. The
+ * `calls` array is read during the call only (host memory).
+ */
+paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydtype, void* ws,
+                              size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -71,13 +71,26 @@ _lib.paro_workspace_bytes.restype = _sz
 _lib.paro_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.paro_w4a16_linear.restype = _i
 _lib.paro_w4a16_linear.argtypes = [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+
+
+class paro_linear_args(ctypes.Structure):
+    """One call of paro_linear_batch (include/paro.h)."""
+    _fields_ = [("rot", ctypes.POINTER(paro_rotation)), ("M", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("x", _vp), ("qweight", _vp), ("scales", _vp), ("zeros", _vp), ("y", _vp)]
+
+
+_lib.paro_linear_batch_workspace_bytes.restype = _sz
+_lib.paro_linear_batch_workspace_bytes.argtypes = [_i, ctypes.POINTER(paro_linear_args)]
+_lib.paro_linear_batch.restype = _i
+_lib.paro_linear_batch.argtypes = [_i, ctypes.POINTER(paro_linear_args), _i, _vp, _sz, _vp]
 _lib.paro_rotated_linear.restype = _i
 _lib.paro_rotated_linear.argtypes = [ctypes.POINTER(paro_rotation), _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp,
                                      _sz, _vp]
 
 EXPORTS = ("paro_status_str", "paro_version", "paro_rotation_bytes", "paro_rotation_encode", "paro_rotation_prepare",
            "paro_pack_weights", "paro_rotate", "paro_workspace_bytes", "paro_w4a16_linear",
-           "paro_rotated_linear")
+           "paro_rotated_linear", "paro_linear_batch_workspace_bytes",
+           "paro_linear_batch")
 
 
 class ParoError(RuntimeError):
@@ -264,9 +277,6 @@ def paro_w4a16_linear(x, qweight, scales, zeros, out_dtype=None, out=None, ws=No
     _want(scales, torch.float16, (N, D // GROUP), "scales")
     _want(zeros, torch.float16, (N, D // GROUP), "zeros")
     y = _linear_out(M, N, out_dtype or torch.float16, x.device, out)
-    need = _lib.paro_workspace_bytes(M, D, N)
-    if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
         _check(_lib.paro_w4a16_linear(M, D, N, _ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), _ydt(y),
                                       _ptr(ws), ws.numel() if ws is not None else 0, _stream_ptr(x.device)),
@@ -293,3 +303,43 @@ def paro_rotated_linear(rot: Rotation, x, qweight, scales, zeros, out_dtype=None
                                         _stream_ptr(x.device)),
                "paro_rotated_linear")
     return y
+
+
+def paro_linear_batch(calls, out_dtype=None, outs=None, ws=None):
+    """Independent linears in as few launches as possible (paro_linear_batch in include/paro.h).
+
+    calls: sequence of (rot, x, qweight, scales, zeros) with rot a Rotation or None (plain INT4
+    linear). Returns the list of outputs (new tensors of out_dtype, float16 by default, unless
+    `outs` gives them)."""
+    torch = _torch()
+    n = len(calls)
+    arr = (paro_linear_args * max(n, 1))()
+    ys, keep = [], []
+    dtype = out_dtype or (outs[0].dtype if outs else torch.float16)
+    device = None
+    for i, (rot, x, qweight, scales, zeros) in enumerate(calls):
+        M, D = int(x.shape[0]), int(x.shape[1])
+        N = int(qweight.shape[0])
+        if rot is not None and rot.D != D:
+            raise ValueError(f"call {i}: x has {D} channels, the transform {rot.D}")
+        _want(x, torch.float16, (M, D), "x")
+        _want(qweight, torch.uint8, (N, D // 2), "qweight")
+        _want(scales, torch.float16, (N, D // GROUP), "scales")
+        _want(zeros, torch.float16, (N, D // GROUP), "zeros")
+        y = _linear_out(M, N, dtype, x.device, outs[i] if outs else None)
+        if y.dtype != dtype:
+            raise TypeError("every output of a batch has the same dtype")
+        device = x.device
+        ys.append(y)
+        keep.append(rot)
+        arr[i] = paro_linear_args(ctypes.pointer(rot.handle) if rot is not None else None, M, D, N, x.data_ptr(),
+                                  qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), y.data_ptr())
+    if n == 0:
+        return ys
+    need = _lib.paro_linear_batch_workspace_bytes(n, arr)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    with torch.cuda.device(device):
+        _check(_lib.paro_linear_batch(n, arr, _ydt(ys[0]), _ptr(ws), ws.numel() if ws is not None else 0,
+                                      _stream_ptr(device)), "paro_linear_batch")
+    return ys

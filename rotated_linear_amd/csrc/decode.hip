@@ -1,31 +1,37 @@
-// Decode-shaped W4A16 linear (M <= 16 tokens) on the matrix cores, optionally
-// with the activation transform fused in front ("ParoQuant: pairwise rotations
-// that survive deployment", section "A rotation small enough to execute": the
-// inverse activation-side transform runs right before the packed INT4 linear).
+// Decode-shaped W4A16 linears (M <= 16 tokens per call) on the matrix cores, one call or a
+// whole batch of calls per launch, with the activation transform optionally run inside the
+// kernel ("ParoQuant: pairwise rotations that survive deployment", section "A rotation small
+// enough to execute": the inverse activation-side transform runs right before the packed
+// INT4 linear).
 //
 //   y[m][n] = sum_g scale[n][g] * sum_{k in g} x'[m][k] * (q[n][k] - z[n][g])
 //
 // HBM-bound design for gfx950:
-//   * persistent workgroups of 4 waves walk 16-row tiles of W; the 4 waves of a
-//     workgroup split a tile's 128-channel groups (g = wave, wave + 4, ...);
-//   * each lane streams one 16-byte chunk (32 channels) of one weight row per
-//     group; PF groups (weights + scale + zero) stay in flight per lane in a
-//     register ring. The ring is software-pipelined as prologue / steady state /
-//     tail so that no load sits under a condition and none is issued past the
-//     end: the compiler's wait counts then stay exact (a group waits only for
-//     its own loads). Per-tile partial sums go to LDS; they are combined and
-//     stored after the loop, so the loop holds no barrier and no global store;
-//   * nibbles -> float16 by AND-OR with the 0x6400 exponent pattern, minus
-//     (1024 + z): the exact integers (q - z) form the B operand of
-//     v_mfma_f32_16x16x32_f16 straight from registers; the group scale is applied
-//     in float32 to each group's MFMA result;
-//   * the A operand (<= 16 rows of x or the transformed x, float16) sits in LDS
-//     chunk-major ([D/8][rows] 16-byte chunks), so the 16 rows a wave reads for
-//     one MFMA are 16 consecutive chunks (no bank conflicts). Plain x arrives by
-//     direct global->LDS loads; the transformed x is written there by the fused
-//     prologue, which runs the K stages once per workgroup in LDS
-//     (rotation_core.h) with the stage records, x and 1/s loaded before the
-//     weights so that waiting for them never waits for the weights.
+//  * one workgroup of 8 waves per CU. A launch carries a table of units (row blocks of the
+//    calls, at most 16 rows, at most 4 with the transform inside) in its kernel arguments;
+//    each workgroup serves one unit: a contiguous range of its 16-row weight tiles;
+//  * the 8 waves form 8 / WPT streams; a stream walks its tiles and its WPT waves split a
+//    tile's 128-channel groups (wave w of the stream takes g = w, w + WPT, ...);
+//  * per group a lane streams one 16-byte chunk (32 nibbles) of one weight row and the 32-bit
+//    words holding its scale and zero. PF groups stay in flight per lane in a register ring,
+//    software-pipelined so that every load is unconditional and the compiler's wait counts
+//    stay exact (a group waits for its own loads only);
+//  * nibbles -> exact float16 (q - z): (u & 0x000F000F) | 0x64006400 is 1024 + q, the
+//    nibbles at bits 4..7 give 1024 + 16 q, brought back by one fused multiply-add with
+//    1/16; the (q - z) words are the B operand of v_mfma_f32_16x16x32_f16 and the group
+//    scale multiplies each group's float32 MFMA result;
+//  * the A operand (the unit's rows of x, or of the transformed x, as float16) is staged once
+//    in LDS chunk-major ([D/8][rows] 16-byte chunks). When a wave has at most 4 groups per
+//    tile it keeps its A fragments in registers for the whole kernel; lanes feeding rows past
+//    the unit's rows read a zero chunk;
+//  * a unit with a transform loads its stage records, x and 1/s ahead of the weights and runs
+//    the K stages in LDS (rotation_core.h) while the weight ring is in flight;
+//  * per-tile partial sums go to LDS and the WPT waves are combined after the loop, so the
+//    loop holds no barrier and no global store.
+#include <string.h>
+
+#include <algorithm>
+
 #include "rotation_core.h"
 
 namespace paro {
@@ -35,343 +41,522 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kFusedX = 4;  // fused: 16-byte x loads per thread issued up front
+constexpr int kThreads = kDecodeThreads;
+constexpr int kWaves = kThreads / 64;
+// transform stages whose records are loaded ahead (fewer for wide rows: registers)
+__host__ __device__ constexpr int ring_stages(int ppt) { return ppt >= 3 ? 4 : 8; }
+constexpr int kFusedX = 4;      // x loads per thread in the transform prologue (rows * D / 8 <= 2048)
+constexpr int kPlainX = 8;      // x loads per thread staging a plain unit (rows * D / 8 <= 4096)
+constexpr int kCUs = 256;       // MI355X compute units: one workgroup each
+constexpr size_t kLdsLimit = 144 * 1024;
 
-__device__ inline uint32_t dq2(uint32_t u, uint32_t zz) {
-  const h2 v = __builtin_bit_cast(h2, (u & 0x000F000Fu) | 0x64006400u) - __builtin_bit_cast(h2, zz);
-  return __builtin_bit_cast(uint32_t, v);
-}
+__host__ __device__ constexpr size_t align1k(size_t v) { return (v + 1023) & ~size_t(1023); }
+__host__ __device__ constexpr int rows_class(int rows) { return rows <= 1 ? 1 : (rows <= 2 ? 2 : 4); }
 
-// 8 nibbles of one 32-bit word -> (q - z) as float16 in the order [0,4,1,5,2,6,3,7]
-__device__ inline h8 dequant_word(uint32_t u, uint32_t zz) {
-  uint4 o;
-  o.x = dq2(u, zz);
-  o.y = dq2(u >> 4, zz);
-  o.z = dq2(u >> 8, zz);
-  o.w = dq2(u >> 12, zz);
-  return __builtin_bit_cast(h8, o);
-}
-
-struct Cursor {  // (tile iteration j, group item i) of a wave's flat work list
-  int j, i;
-  __device__ inline void next(int gw) {
-    if (++i == gw) {
-      i = 0;
-      ++j;
-    }
-  }
-};
-
-// LDS layout shared by kernel and launcher.
-struct DecodeLds {
-  size_t rot, xs, red, total;
-  __host__ __device__ static DecodeLds make(bool fused, int mr, int M, int D, int max_tiles) {
-    DecodeLds L;
-    const int rows = fused ? mr : M;
-    L.rot = 0;
-    L.xs = fused ? size_t(mr) * D * 4 : 0;
-    L.red = L.xs + ((size_t(rows) * D * 2 + 1023) & ~size_t(1023));
-    L.total = L.red + size_t(max_tiles) * kWaves * 64 * 16;
+// LDS layout of a unit: [1/s (transform only)] [rows in float32 (transform only)] [x chunks].
+// The x chunk area holds D/8 * rows chunks followed by one zero chunk.
+struct UnitLds {
+  size_t isv, rot, xs, end;
+  __host__ __device__ static UnitLds make(bool fused, int rows, int D) {
+    UnitLds L;
+    L.isv = 0;
+    L.rot = fused ? align1k(size_t(D) * 4) : 0;
+    L.xs = fused ? L.rot + align1k(size_t(rows_class(rows)) * D * 4) : 0;
+    L.end = L.xs + (size_t(D / 8) * rows + 1) * 16;
     return L;
   }
 };
 
-template <bool FUSED, int MR, int PPT, int PD, bool EXACT, bool XPERM, int PF>
-__global__ __launch_bounds__(kThreads) void decode_kernel(int M, int D, int N, int K, const uint16_t* __restrict__ x,
-                                                           const uint8_t* __restrict__ qweight,
-                                                           const uint16_t* __restrict__ scales,
-                                                           const uint16_t* __restrict__ zeros, void* __restrict__ y,
-                                                           int ydtype, const PairRec* __restrict__ recs,
-                                                           const float* __restrict__ inv_s) {
+__host__ __device__ constexpr int ring_depth(int gw) { return gw == 3 ? 9 : 8; }
+
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
+
+// 8 nibbles of one 32-bit word -> exact (q - z) as float16 in the order [0,4,1,5,2,6,3,7].
+// zlo = -(1024 + z) and zhi = -(64 + z), both as float16 pairs.
+__device__ inline h8 dequant_word(uint32_t u, h2 zlo, h2 zhi, uint32_t m0, uint32_t m1, uint32_t e) {
+  const h2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const uint32_t v = u >> 8;
+  const h2 a0 = __builtin_bit_cast(h2, and_or(u, m0, e)) + zlo;                                        // 0, 4
+  const h2 a1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(u, m1, e)), sixteenth, zhi);  // 1, 5
+  const h2 a2 = __builtin_bit_cast(h2, and_or(v, m0, e)) + zlo;                                        // 2, 6
+  const h2 a3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(v, m1, e)), sixteenth, zhi);  // 3, 7
+  const uint4 o = {__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                   __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)};
+  return __builtin_bit_cast(h8, o);
+}
+
+// An empty statement that makes v look redefined here: code computed from v stays below it.
+__device__ inline void pin(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+__device__ inline void pin(float4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+
+__device__ inline h8 decode_order(h8 a) { return __builtin_shufflevector(a, a, 0, 4, 1, 5, 2, 6, 3, 7); }
+
+// The transform of a unit's rows inside the kernel: x (already in registers) -> float32 rows in
+// LDS, the K stages, then x' = rows * (1/s) as float16 chunks in the decode order.
+template <int R, int PPT, int PD>
+__device__ inline void unit_transform(StageRing<kThreads, PPT, PD, false, true>& ring, float* rot, float* isl,
+                                      uint4* xs, const uint4 (&xv)[kFusedX], const float4 (&iv)[2], int rows, int D,
+                                      int K, int tid, const PairRec* __restrict__ recs) {
+  const int chunks = D / 8, xtotal = chunks * rows;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (tid + u * kThreads < D / 4) reinterpret_cast<float4*>(isl)[tid + u * kThreads] = iv[u];
+#pragma unroll
+  for (int u = 0; u < kFusedX; ++u) {
+    const int e = tid + u * kThreads;
+    if (e < xtotal) {
+      const int m = e / chunks, c = e - m * chunks;
+      const uint32_t w[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        rot[(c * 8 + t) * R + m] =
+            static_cast<float>(__builtin_bit_cast(_Float16, uint16_t((t & 1) ? w[t >> 1] >> 16 : w[t >> 1])));
+    }
+  }
+  __syncthreads();
+  if (K > 0) ring_run_short<R>(ring, rot, K, D / 2, tid, recs);  // K <= 8; ends with a barrier
+  for (int e = tid; e < xtotal; e += kThreads) {
+    const int c = e / rows, m = e - c * rows;
+    _Float16 hv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      hv[nib_slot(t)] = static_cast<_Float16>(rot[(c * 8 + t) * R + m] * isl[c * 8 + t]);
+    xs[e] = *reinterpret_cast<const uint4*>(hv);
+  }
+}
+
+// PPT: transform pairs per thread per stage; PPT > 0: every unit of the launch runs its
+// transform inside the kernel, PPT == 0: every unit is a plain linear.
+// GW: groups per wave per tile when the A fragments live in registers (0: read from LDS).
+// WPT: waves per tile.
+template <int PPT, int GW, int WPT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  constexpr int NQ = kWaves / WPT;
+  constexpr int PF = ring_depth(GW);
+  constexpr int TPR = GW > 0 ? PF / GW : 1;
+  constexpr int PD = ring_stages(PPT);
+  static_assert(GW == 0 || PF % GW == 0, "the ring must hold whole tiles");
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, h = lane >> 4;
-  const int G = D / PARO_GROUP;
-  const int gw = (G + kWaves - 1) / kWaves;  // group items per wave per tile (uniform)
-  const int tiles = (N + 15) / 16;
-  const int my_tiles = (tiles - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
-  const int max_tiles = (tiles + int(gridDim.x) - 1) / int(gridDim.x);
-  const int F = my_tiles * gw;  // items of every wave of this workgroup
-  const int rows = FUSED ? MR : M;
-  const DecodeLds L = DecodeLds::make(FUSED, MR, M, D, max_tiles);
-  _Float16* xs = reinterpret_cast<_Float16*>(smem + L.xs);  // [D/8][rows] x 8 halves
-  f4* red = reinterpret_cast<f4*>(smem + L.red);             // [my_tiles][kWaves][64]
-  const int chunks = D / 8;
-  const int xtotal = chunks * rows;
+  const int q = wave / WPT, wq = wave - q * WPT;
+  const int D = args.D, G = D / PARO_GROUP, chunks = D / 8;
 
-  // ---- fused: stage records, x rows and 1/s first (waiting for them never waits for weights)
-  StageRing<kThreads, PPT, PD, EXACT> ring;
-  uint4 xv[FUSED ? kFusedX : 1];
-  float4 isv[FUSED ? 2 * kFusedX : 1];
-  if constexpr (FUSED) {
-    if (K > 0) ring_prime(ring, K, D / 2, tid, recs);
+  // ---- this workgroup's unit and tile range
+  const int b = int(blockIdx.x);
+  int ui = 0;
 #pragma unroll
-    for (int u = 0; u < kFusedX; ++u) {
-      int e = tid + u * kThreads;
-      e = e < xtotal ? e : xtotal - 1;
-      const int m = e / chunks, c = e - m * chunks;
-      const int mc = m < M ? m : M - 1;
-      xv[u] = *reinterpret_cast<const uint4*>(x + size_t(mc) * D + size_t(c) * 8);
-      // 1/s of the chunk this thread writes in the transformed-x phase (entry e = c' * MR + m')
-      const int ec = e / MR;
-      isv[2 * u] = *reinterpret_cast<const float4*>(inv_s + size_t(ec) * 8);
-      isv[2 * u + 1] = *reinterpret_cast<const float4*>(inv_s + size_t(ec) * 8 + 4);
+  for (int i = 1; i < kDecodeMaxUnits; ++i)
+    if (i < args.nunits && b >= int(args.first_block[i])) ui = i;
+  const DecodeUnit& U = args.u[ui];
+  const int N = U.N, rows = U.rows, K = U.K;
+  const uint8_t* __restrict__ qw = U.qw;
+  const uint32_t* __restrict__ sc32 = reinterpret_cast<const uint32_t*>(U.sc);
+  const uint32_t* __restrict__ zr32 = reinterpret_cast<const uint32_t*>(U.zr);
+  const int tiles = (N + 15) >> 4;
+  const int t_begin = (b - int(args.first_block[ui])) * U.tpb;
+  const int my_tiles = min(U.tpb, tiles - t_begin);              // >= 1 by construction
+  const int qt = my_tiles > q ? (my_tiles - q + NQ - 1) / NQ : 0;  // tiles of this wave's stream
+  const int gw = GW > 0 ? GW : (G + WPT - 1) / WPT;
+  constexpr bool fused = PPT > 0;
+  const UnitLds L = UnitLds::make(fused, rows, D);
+  uint4* xs = reinterpret_cast<uint4*>(smem + L.xs);
+  const int xtotal = chunks * rows;
+  const int zero_idx = xtotal;
+  if (tid == 0) xs[zero_idx] = uint4{0u, 0u, 0u, 0u};
+
+  // ---- loads the weights must not delay (issued first, so waiting for them never waits for
+  // a weight): transform records, 1/s and x, or the plain x
+  StageRing<kThreads, (PPT > 0 ? PPT : 1), PD, false, true> ring;  // PPT = ceil(D/2 / 512)
+  uint4 xv[kFusedX];
+  float4 iv[2];
+  uint4 pv[kPlainX];
+  if constexpr (fused) {
+    {
+      ring_prime(ring, K, D / 2, tid, U.rec);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        int e = tid + u * kThreads;
+        e = e < D / 4 ? e : D / 4 - 1;
+        iv[u] = reinterpret_cast<const float4*>(U.inv_s)[e];
+      }
+#pragma unroll
+      for (int u = 0; u < kFusedX; ++u) {
+        int e = tid + u * kThreads;
+        e = e < xtotal ? e : xtotal - 1;
+        const int m = e / chunks, c = e - m * chunks;
+        xv[u] = *reinterpret_cast<const uint4*>(U.x + size_t(m) * D + size_t(c) * 8);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nx = (xtotal + kThreads - 1) / kThreads;  // plain: x loads per thread (uniform)
+  if constexpr (!fused) {
+#pragma unroll
+    for (int u = 0; u < kPlainX; ++u) {
+      if (u < nx) {
+        int e = tid + u * kThreads;  // LDS chunk e = c * rows + m
+        e = e < xtotal ? e : xtotal - 1;
+        const int c = e / rows, m = e - c * rows;
+        pv[u] = *reinterpret_cast<const uint4*>(U.x + size_t(m) * D + size_t(c) * 8);
+      }
+    }
   }
 
-  // ---- weight ring: prologue issues items 0..PF-1 (clamped when F < PF)
-  uint4 wq[PF];
-  uint32_t sq[PF], zq[PF];
-  const uint32_t* scales32 = reinterpret_cast<const uint32_t*>(scales);
-  const uint32_t* zeros32 = reinterpret_cast<const uint32_t*>(zeros);
-  Cursor ci{0, 0};
-  auto issue = [&](uint4& wslot, uint32_t& sslot, uint32_t& zslot) {
-    const int tile = int(blockIdx.x) + (ci.j < my_tiles ? ci.j : my_tiles - 1) * int(gridDim.x);
-    int n = tile * 16 + nl;
+  // ---- weight ring prologue: the first PF groups of this wave (nothing may move across it:
+  // waiting for the loads above must not wait for these)
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t rowb = uint32_t(D) / 2;
+  const int jmax = qt > 0 ? qt - 1 : 0;
+  const int row0 = (t_begin + q) * 16 + nl;  // this lane's weight row in the stream's first tile
+  uint4 wr[PF];
+  uint32_t sr[PF], zr[PF];
+  auto issue = [&](int j, int g, uint4& w, uint32_t& sw, uint32_t& zw) {
+    j = j < jmax ? j : jmax;
+    int n = row0 + j * (NQ * 16);
     n = n < N ? n : N - 1;
-    int g = wave + kWaves * ci.i;
     g = g < G ? g : G - 1;
-    wslot = *reinterpret_cast<const uint4*>(qweight + size_t(n) * (D / 2) + size_t(g) * 64 + h * 16);
-    // scale and zero: the aligned 32-bit word holding them (the half is picked at use)
-    const size_t gi = size_t(n) * G + g;
-    sslot = scales32[gi >> 1];
-    zslot = zeros32[gi >> 1];
-    ci.next(gw);
+    w = *reinterpret_cast<const uint4*>(qw + (uint32_t(n) * rowb + uint32_t(g) * 64u + uint32_t(h) * 16u));
+    const uint32_t gi = uint32_t(n) * uint32_t(G) + uint32_t(g);
+    sw = sc32[gi >> 1];
+    zw = zr32[gi >> 1];
   };
 #pragma unroll
-  for (int s = 0; s < PF; ++s) issue(wq[s], sq[s], zq[s]);
-
-  if constexpr (FUSED) {
-    float* rot = reinterpret_cast<float*>(smem + L.rot);  // [D][MR]
-    const int P = D / 2;
-    auto put = [&](int e, const uint4& v) {
-      const int m = e / chunks, c = e - m * chunks;
-      const _Float16* hv = reinterpret_cast<const _Float16*>(&v);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) rot[(c * 8 + t) * MR + m] = static_cast<float>(hv[t]);
-    };
-#pragma unroll
-    for (int u = 0; u < kFusedX; ++u) {
-      const int e = tid + u * kThreads;
-      if (e < xtotal) put(e, xv[u]);
-    }
-    for (int base = kFusedX * kThreads; base < xtotal; base += kThreads) {  // MR * D > 8192 only
-      const int e = base + tid;
-      if (e < xtotal) {
-        const int m = e / chunks, c = e - m * chunks;
-        const int mc = m < M ? m : M - 1;
-        put(e, *reinterpret_cast<const uint4*>(x + size_t(mc) * D + size_t(c) * 8));
-      }
-    }
-    __syncthreads();
-    if (K > 0) ring_run<MR>(ring, rot, K, P, tid, recs);
-    // transformed x -> chunk-major LDS slots e = c * MR + m, scaled by 1/s, nibble order
-    auto put_x = [&](int e, float4 i0, float4 i1) {
-      const int c = e / MR, m = e - c * MR;
-      const float is[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-      _Float16 hv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) hv[nib_slot(u)] = static_cast<_Float16>(rot[(c * 8 + u) * MR + m] * is[u]);
-      *reinterpret_cast<uint4*>(xs + size_t(e) * 8) = *reinterpret_cast<const uint4*>(hv);
-    };
-#pragma unroll
-    for (int u = 0; u < kFusedX; ++u) {
-      const int e = tid + u * kThreads;
-      if (e < xtotal) put_x(e, isv[2 * u], isv[2 * u + 1]);
-    }
-    for (int base = kFusedX * kThreads; base < xtotal; base += kThreads) {
-      const int e = base + tid;
-      if (e < xtotal) {
-        const int c = e / MR;
-        put_x(e, *reinterpret_cast<const float4*>(inv_s + size_t(c) * 8),
-              *reinterpret_cast<const float4*>(inv_s + size_t(c) * 8 + 4));
-      }
-    }
-  } else {
-    (void)ring;
-    (void)xv;
-    (void)isv;
-    // direct global->LDS: the wave's 64 lanes fill one 1 KB block of chunk-major slots
+  for (int s = 0; s < PF; ++s) {
+    if constexpr (GW > 0)
+      issue(s / GW, wq + WPT * (s % GW), wr[s], sr[s], zr[s]);
+    else
+      issue(s / gw, wq + WPT * (s % gw), wr[s], sr[s], zr[s]);
+    // keep the refill order (weights, scale, zero per group): the loop's wait counts assume it
     __builtin_amdgcn_sched_barrier(0);
-    const int nblk = (xtotal + 63) / 64;
-    for (int b = wave; b < nblk; b += kWaves) {
-      int s = b * 64 + lane;
-      s = s < xtotal ? s : xtotal - 1;
-      const int c = s / M, m = s - c * M;
-      __builtin_amdgcn_global_load_lds(x + size_t(m) * D + size_t(c) * 8, smem + L.xs + size_t(b) * 1024, 16, 0,
-                                       0);
+  }
+  // The staged values are first used here: nothing computed from them may be hoisted above
+  // the weight loads (each empty statement makes its operand look redefined at this point).
+  if constexpr (fused) {
+#pragma unroll
+    for (int u = 0; u < kFusedX; ++u) pin(xv[u]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) pin(iv[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPlainX; ++u)
+      if (u < nx) pin(pv[u]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- stage the A operand
+  if constexpr (fused) {
+    {
+      float* rot = reinterpret_cast<float*>(smem + L.rot);
+      float* isl = reinterpret_cast<float*>(smem + L.isv);
+      const int R = rows_class(rows);
+      if (R == 1)
+        unit_transform<1>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, U.rec);
+      else if (R == 2)
+        unit_transform<2>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, U.rec);
+      else
+        unit_transform<4>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, U.rec);
     }
-    // the direct loads land in LDS asynchronously: wait for them before the barrier
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if constexpr (!fused) {
+    const bool perm = !U.xperm;
+#pragma unroll
+    for (int u = 0; u < kPlainX; ++u) {
+      const int e = tid + u * kThreads;
+      if (u < nx && e < xtotal) {
+        const h8 a = __builtin_bit_cast(h8, pv[u]);
+        xs[e] = __builtin_bit_cast(uint4, perm ? decode_order(a) : a);
+      }
+    }
   }
   __syncthreads();
+
+  h8 areg[GW > 0 ? GW : 1][4];
+  if constexpr (GW > 0) {
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int g = wq + WPT * i;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int idx = (nl < rows && g < G) ? (g * 16 + 4 * h + kk) * rows + nl : zero_idx;
+        areg[i][kk] = __builtin_bit_cast(h8, xs[idx]);
+      }
+    }
+  }
 
   // ---- stream the weights
-  const int arow = nl < rows ? nl : rows - 1;  // A row this lane feeds (rows >= M read as zero)
-  const bool arow_ok = nl < M;
-  const _Float16* xa = xs + size_t(arow) * 8 + size_t(h) * 4 * rows * 8;  // chunk 4h of group 0
-  const size_t group_stride = size_t(16) * rows * 8;                     // 16 chunks per group
-  const size_t chunk_stride = size_t(rows) * 8;
+  f4* red = reinterpret_cast<f4*>(smem + args.red_off);  // [tile][WPT][RL] partial sums
+  const int RL = 16 * ((rows + 3) >> 2);                 // lanes holding rows < `rows`
+  const uint32_t km0 = 0x000F000Fu, km1 = 0x00F000F0u, ke = 0x64006400u;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  Cursor cc{0, 0};
 
-  auto consume = [&](int f, uint4 wv4, uint32_t sw, uint32_t zw) {
-    const int g = wave + kWaves * cc.i;
-    if (f < F && g < G) {  // uniform per wave; no global load inside
-      int nn = (int(blockIdx.x) + cc.j * int(gridDim.x)) * 16 + nl;
-      nn = nn < N ? nn : N - 1;
-      const int hi = ((nn & G) ^ g) & 1;  // parity of nn*G + g: which half of the fetched word
-      const _Float16 z = hi ? __builtin_bit_cast(h2, zw).y : __builtin_bit_cast(h2, zw).x;
-      const _Float16 zz = static_cast<_Float16>(1024.0f) + z;
-      const uint32_t zz2 = uint32_t(__builtin_bit_cast(uint16_t, zz)) * 0x10001u;
-      const uint32_t wv[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
-      f4 accg = {0.f, 0.f, 0.f, 0.f};
+  auto mac = [&](int j, int g, const h8(&a)[4], const uint4& w, uint32_t sw, uint32_t zw) {
+    int n = row0 + j * (NQ * 16);
+    n = n < N ? n : N - 1;
+    const bool hi = ((uint32_t(n) * uint32_t(G) + uint32_t(g)) & 1u) != 0;
+    const _Float16 z = __builtin_bit_cast(_Float16, uint16_t(hi ? zw >> 16 : zw));
+    const _Float16 sc = __builtin_bit_cast(_Float16, uint16_t(hi ? sw >> 16 : sw));
+    const _Float16 zl = -(static_cast<_Float16>(1024.0f) + z), zh = -(static_cast<_Float16>(64.0f) + z);
+    const h2 zlo = {zl, zl}, zhi = {zh, zh};
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    f4 accg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        h8 a = *reinterpret_cast<const h8*>(xa + size_t(g) * group_stride + ww * chunk_stride);
-        if constexpr (!XPERM) a = __builtin_shufflevector(a, a, 0, 4, 1, 5, 2, 6, 3, 7);
-        a = arow_ok ? a : h8{};
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant_word(wv[ww], zz2), accg, 0, 0, 0);
-      }
-      const float sc = static_cast<float>(hi ? __builtin_bit_cast(h2, sw).y : __builtin_bit_cast(h2, sw).x);
-      acc += sc * accg;
-    }
-    const int jt = cc.j;
-    cc.next(gw);
-    if (cc.i == 0 && jt < my_tiles) {  // tile done: park this wave's partial sums (LDS only)
-      red[(jt * kWaves + wave) * 64 + lane] = acc;
-      acc = f4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int kk = 0; kk < 4; ++kk)
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kk], dequant_word(wv[kk], zlo, zhi, km0, km1, ke), accg, 0,
+                                                    0, 0);
+    acc += static_cast<float>(sc) * accg;
+  };
+  auto park = [&](int j) {  // the wave's partial sums of stream tile j -> LDS
+    if (lane < RL) red[((q + NQ * j) * WPT + wq) * RL + lane] = acc;
+    acc = f4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // steady state: rounds whose refills are all real items (no condition around any load)
-  const int steady = F >= 2 * PF ? (F - PF) / PF : 0;
-  for (int r = 0; r < steady; ++r) {
+  if constexpr (GW > 0) {
+    const int rounds = (qt + TPR - 1) / TPR;
+    auto step = [&](int r, int s, bool refill) {
+      const int j = r * TPR + s / GW, i = s % GW, g = wq + WPT * i;
+      if (j < qt) {
+        if (g < G) mac(j, g, areg[i], wr[s], sr[s], zr[s]);
+        if (i == GW - 1) park(j);
+      }
+      if (refill) issue(j + TPR, g, wr[s], sr[s], zr[s]);
+    };
+    for (int r = 0; r + 1 < rounds; ++r) {
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-      consume(r * PF + s, wq[s], sq[s], zq[s]);
-      issue(wq[s], sq[s], zq[s]);
+      for (int s = 0; s < PF; ++s) step(r, s, true);
     }
-  }
-  // tail: at most 2 * PF - 1 items; refill only while real items remain
-  const int base = steady * PF;
+    const int rl = rounds > 0 ? rounds - 1 : 0;
 #pragma unroll
-  for (int s = 0; s < PF; ++s) {
-    consume(base + s, wq[s], sq[s], zq[s]);
-    if (base + s + PF < F) issue(wq[s], sq[s], zq[s]);
-  }
+    for (int s = 0; s < PF; ++s) step(rl, s, false);
+  } else {
+    const int F = qt * gw;
+    const int rounds = (F + PF - 1) / PF;
+    int cj = 0, cg = 0;                          // consume cursor: stream tile, group item
+    int ij = PF / gw, ig = PF - (PF / gw) * gw;  // issue cursor (the prologue issued PF items)
+    auto step = [&](int s, bool refill) {
+      const int g = wq + WPT * cg;
+      if (cj < qt) {
+        if (g < G) {
+          h8 a[4];
 #pragma unroll
-  for (int s = 0; s < PF; ++s) {
-    if (base + PF + s < F) consume(base + PF + s, wq[s], sq[s], zq[s]);
+          for (int kk = 0; kk < 4; ++kk)
+            a[kk] = __builtin_bit_cast(h8, xs[nl < rows ? (g * 16 + 4 * h + kk) * rows + nl : zero_idx]);
+          mac(cj, g, a, wr[s], sr[s], zr[s]);
+        }
+        if (cg == gw - 1) park(cj);
+      }
+      if (++cg == gw) {
+        cg = 0;
+        ++cj;
+      }
+      if (refill) {
+        issue(ij, wq + WPT * ig, wr[s], sr[s], zr[s]);
+        if (++ig == gw) {
+          ig = 0;
+          ++ij;
+        }
+      }
+    };
+    for (int r = 0; r + 1 < rounds; ++r) {
+#pragma unroll
+      for (int s = 0; s < PF; ++s) step(s, true);
+    }
+#pragma unroll
+    for (int s = 0; s < PF; ++s) step(s, false);
   }
   __syncthreads();
 
-  // ---- combine the 4 waves and store (16 consecutive columns per row)
-  for (int e = tid; e < my_tiles * 256; e += kThreads) {
-    const int jt = e >> 8, m = (e >> 4) & 15, c = e & 15;
-    const int ln = (m >> 2) * 16 + c, r = m & 3;
+  // ---- combine the WPT waves of each tile and store
+  const int per_tile = rows * 16;
+  for (int e = tid; e < my_tiles * per_tile; e += kThreads) {
+    const int tl = e / per_tile, rem = e - tl * per_tile;
+    const int m = rem >> 4, c = rem & 15;
+    const int ln = (m >> 2) * 16 + c;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[(jt * kWaves + w) * 64 + ln][r];
-    const int n = (int(blockIdx.x) + jt * int(gridDim.x)) * 16 + c;
-    if (m < M && n < N) {
-      if (ydtype == PARO_F32)
-        static_cast<float*>(y)[size_t(m) * N + n] = v;
+    for (int w = 0; w < WPT; ++w) v += red[(tl * WPT + w) * RL + ln][m & 3];
+    const int n = (t_begin + tl) * 16 + c;
+    if (n < N) {
+      if (args.ydtype == PARO_F32)
+        static_cast<float*>(U.y)[size_t(m) * N + n] = v;
       else
-        static_cast<_Float16*>(y)[size_t(m) * N + n] = static_cast<_Float16>(v);
+        static_cast<_Float16*>(U.y)[size_t(m) * N + n] = static_cast<_Float16>(v);
     }
   }
 }
 
-template <bool FUSED, int MR, int PPT, int PD, bool EXACT, bool XPERM>
-hipError_t launch_cfg(const DevRot* rot, int M, int D, int N, const uint16_t* x, const uint8_t* qweight,
-                      const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, int grid,
-                      hipStream_t st) {
-  const int tiles = (N + 15) / 16;
-  const int max_tiles = (tiles + grid - 1) / grid;
-  const size_t lds = DecodeLds::make(FUSED, MR, M, D, max_tiles).total;
-  const int items = max_tiles * ((D / PARO_GROUP + kWaves - 1) / kWaves);
-  // ring depth: 8 groups in flight, 4 when a wave has few items (fewer wasted loads)
-  auto go = [&](auto kernel) -> hipError_t {
-    if (lds > 64 * 1024) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, st, M, D, N, rot ? rot->K : 0, x, qweight, scales,
-                       zeros, y, ydtype, rot ? rot->rec : nullptr, rot ? rot->inv_s : nullptr);
-    return hipGetLastError();
-  };
-  if (items <= 4) return go(decode_kernel<FUSED, MR, PPT, PD, EXACT, XPERM, 4>);
-  return go(decode_kernel<FUSED, MR, PPT, PD, EXACT, XPERM, 8>);
+// ------------------------------------------------------------------------------------------
+// host side: units, workgroups, LDS and the kernel instantiation of a launch
+
+struct Plan {
+  DecodeArgs args;
+  int grid, ppt, gw, wpt;
+  size_t lds;
+};
+
+int plain_rows_max(int D) {
+  const int by_lds = (kPlainX * kThreads - 1) / (D / 8);  // a unit's x chunks: kPlainX per thread
+  return by_lds < 1 ? 1 : (by_lds > kDecodeMaxM ? kDecodeMaxM : by_lds);
 }
 
-template <int MR, int PPT, int PD>
-hipError_t launch_fused_exact(const DevRot& rot, int M, int D, int N, const uint16_t* x, const uint8_t* qweight,
-                              const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, int grid,
-                              hipStream_t st) {
-  if (D / 2 == PPT * kThreads)
-    return launch_cfg<true, MR, PPT, PD, true, true>(&rot, M, D, N, x, qweight, scales, zeros, y, ydtype, grid, st);
-  return launch_cfg<true, MR, PPT, PD, false, true>(&rot, M, D, N, x, qweight, scales, zeros, y, ydtype, grid, st);
-}
-
-template <int MR>
-hipError_t launch_fused(const DevRot& rot, int M, int D, int N, const uint16_t* x, const uint8_t* qweight,
-                        const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, int grid,
-                        hipStream_t st) {
-  // pairs per thread per stage, and stages kept in flight (<= ~96 registers of ring)
-  const int ppt = (D / 2 + kThreads - 1) / kThreads;
-#define PARO_FUSED(PPT, PD) \
-  if (ppt <= PPT) return launch_fused_exact<MR, PPT, PD>(rot, M, D, N, x, qweight, scales, zeros, y, ydtype, grid, st)
-  PARO_FUSED(1, 8);
-  PARO_FUSED(2, 8);
-  PARO_FUSED(3, 8);
-  PARO_FUSED(4, 8);
-  PARO_FUSED(6, 4);
-  PARO_FUSED(8, 4);
-  PARO_FUSED(12, 2);
-  if constexpr (MR <= 2) {  // four rows of D > 6144 never fit the fused LDS budget
-    PARO_FUSED(16, 2);
-    PARO_FUSED(24, 1);
-    PARO_FUSED(32, 1);
+template <int PPT, int GW, int WPT>
+hipError_t go(const Plan& p, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&decode_kernel<PPT, GW, WPT>);
+  if (p.lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(p.lds));
+    if (e != hipSuccess) return e;
   }
-#undef PARO_FUSED
+  hipLaunchKernelGGL((decode_kernel<PPT, GW, WPT>), dim3(p.grid), dim3(kThreads), p.lds, st, p.args);
+  return hipGetLastError();
+}
+
+// Instantiated combinations: with the A fragments in registers a wave covers GW * WPT groups,
+// i.e. D <= 128 * GW * WPT, and a transform takes PPT = ceil(D / 1024) pairs per thread.
+template <int WPT, int GW>
+hipError_t go_ppt(const Plan& p, hipStream_t st) {
+  constexpr int maxp = GW == 0 ? 0 : (GW * WPT + 7) / 8;
+  switch (p.ppt) {
+    case 0:
+      return go<0, GW, WPT>(p, st);
+    case 1:
+      if constexpr (maxp >= 1) return go<1, GW, WPT>(p, st);
+      break;
+    case 2:
+      if constexpr (maxp >= 2) return go<2, GW, WPT>(p, st);
+      break;
+    case 3:
+      if constexpr (maxp >= 3) return go<3, GW, WPT>(p, st);
+      break;
+    case 4:
+      if constexpr (maxp >= 4) return go<4, GW, WPT>(p, st);
+      break;
+    default:
+      break;
+  }
   return hipErrorInvalidValue;
 }
 
-int decode_grid(bool fused, int N) {
-  // persistent grid: one workgroup per CU when each workgroup recomputes the transform,
-  // two per CU otherwise; never more workgroups than 16-row tiles
-  const int tiles = (N + 15) / 16;
-  const int cap = fused ? 256 : 512;
-  return tiles < cap ? tiles : cap;
+hipError_t dispatch(const Plan& p, hipStream_t st) {
+  if (p.wpt == 4) {
+    switch (p.gw) {
+      case 1: return go_ppt<4, 1>(p, st);
+      case 2: return go_ppt<4, 2>(p, st);
+      case 3: return go_ppt<4, 3>(p, st);
+      case 4: return go_ppt<4, 4>(p, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (p.gw) {
+    case 0: return go_ppt<8, 0>(p, st);
+    case 1: return go_ppt<8, 1>(p, st);
+    case 2: return go_ppt<8, 2>(p, st);
+    case 3: return go_ppt<8, 3>(p, st);
+    case 4: return go_ppt<8, 4>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+struct UnitSrc {
+  DecodeUnit u;
+  int tiles;
+};
+
+// Plan one launch over units[0..n): workgroups per unit in proportion to its tiles.
+bool plan_launch(int D, int ydtype, const UnitSrc* units, int n, Plan& p) {
+  const int G = D / PARO_GROUP;
+  long total = 0;
+  bool any_fused = false;
+  for (int i = 0; i < n; ++i) {
+    total += units[i].tiles;
+    any_fused |= units[i].u.rec != nullptr;
+  }
+  // waves per tile depend on D only, so an output's float32 sums do not depend on which other
+  // calls share the launch
+  p.wpt = G <= 16 ? 4 : 8;
+  const int gw = (G + p.wpt - 1) / p.wpt;
+  p.gw = gw <= 4 ? gw : 0;
+  p.ppt = any_fused ? (D + 1023) / 1024 : 0;
+  long budget = kCUs;  // workgroups to spread; grows only if the LDS does not fit
+  for (;;) {
+    memset(&p.args, 0, sizeof(p.args));
+    p.args.D = D;
+    p.args.ydtype = ydtype;
+    p.args.nunits = n;
+    long grid = 0;
+    size_t xs_end = 0, red = 0;
+    for (int i = 0; i < n; ++i) {
+      const int t = units[i].tiles;
+      long nb = (budget * t + total / 2) / total;
+      nb = nb < 1 ? 1 : (nb > t ? t : nb);
+      const int tpb = int((t + nb - 1) / nb);
+      nb = (t + tpb - 1) / tpb;
+      p.args.u[i] = units[i].u;
+      p.args.u[i].tpb = tpb;
+      p.args.first_block[i] = int(grid);
+      grid += nb;
+      const UnitLds L = UnitLds::make(units[i].u.rec != nullptr, units[i].u.rows, D);
+      xs_end = L.end > xs_end ? L.end : xs_end;
+      const size_t r = size_t(tpb) * p.wpt * (16 * ((units[i].u.rows + 3) / 4)) * 16;
+      red = r > red ? r : red;
+    }
+    p.args.red_off = int(align1k(xs_end));
+    p.lds = align1k(xs_end) + red;
+    p.grid = int(grid);
+    if (p.lds <= kLdsLimit && grid <= 65535) return true;
+    if (budget >= total || grid > 65535) return false;
+    budget *= 2;  // more workgroups, fewer tiles each
+  }
 }
 
 }  // namespace
 
-size_t decode_lds_bytes(bool fused, int M, int D, int N) {
-  const int mr = M <= 1 ? 1 : (M <= 2 ? 2 : 4);
-  const int grid = decode_grid(fused, N);
-  const int tiles = (N + 15) / 16;
-  return DecodeLds::make(fused, mr, M, D, grid > 0 ? (tiles + grid - 1) / grid : 1).total;
+bool decode_takes(int K, int M, int D, int N) {
+  if (M < 1 || M > kDecodeMaxM || N < 1 || D < PARO_GROUP || D > PARO_MAX_D || D % PARO_GROUP) return false;
+  return K < 0 || (D <= kDecodeFusedMaxD && K <= kUnrolledStages);
 }
 
-hipError_t launch_decode(const DevRot* rot, int M, int D, int N, const uint16_t* x, bool x_nibble_order,
-                         const uint8_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype,
-                         hipStream_t st) {
-  if (M < 1 || M > 16 || (rot && M > 4)) return hipErrorInvalidValue;
-  const int grid = decode_grid(rot != nullptr, N);
-  if (rot) {
-    if (M == 1) return launch_fused<1>(*rot, M, D, N, x, qweight, scales, zeros, y, ydtype, grid, st);
-    if (M == 2) return launch_fused<2>(*rot, M, D, N, x, qweight, scales, zeros, y, ydtype, grid, st);
-    return launch_fused<4>(*rot, M, D, N, x, qweight, scales, zeros, y, ydtype, grid, st);
+hipError_t launch_decode(int D, int ydtype, const DecodeCall* calls, int count, hipStream_t st) {
+  std::vector<UnitSrc> units;
+  const size_t ysize = ydtype == PARO_F32 ? 4 : 2;
+  for (int c = 0; c < count; ++c) {
+    const DecodeCall& k = calls[c];
+    if (!decode_takes(k.rot ? k.rot->K : -1, k.M, D, k.N) || (k.rot && k.rot->D != D)) return hipErrorInvalidValue;
+    const int step = k.rot ? 4 : plain_rows_max(D);
+    for (int r0 = 0; r0 < k.M; r0 += step) {
+      UnitSrc s;
+      memset(&s, 0, sizeof(s));
+      s.u.x = k.x + size_t(r0) * D;
+      s.u.qw = k.qweight;
+      s.u.sc = k.scales;
+      s.u.zr = k.zeros;
+      s.u.y = static_cast<char*>(k.y) + size_t(r0) * size_t(k.N) * ysize;
+      s.u.rec = k.rot ? k.rot->rec : nullptr;
+      s.u.inv_s = k.rot ? k.rot->inv_s : nullptr;
+      s.u.N = k.N;
+      s.u.K = k.rot ? k.rot->K : 0;
+      s.u.rows = k.M - r0 < step ? k.M - r0 : step;
+      s.u.xperm = (!k.rot && k.x_nibble_order) ? 1 : 0;
+      s.tiles = (k.N + 15) / 16;
+      units.push_back(s);
+    }
   }
-  if (x_nibble_order)
-    return launch_cfg<false, 16, 1, 1, false, true>(nullptr, M, D, N, x, qweight, scales, zeros, y, ydtype, grid, st);
-  return launch_cfg<false, 16, 1, 1, false, false>(nullptr, M, D, N, x, qweight, scales, zeros, y, ydtype, grid, st);
+  // units with the transform inside and plain units run in separate launches
+  std::stable_partition(units.begin(), units.end(), [](const UnitSrc& s) { return s.u.rec != nullptr; });
+  size_t u0 = 0;
+  while (u0 < units.size()) {
+    const bool rot = units[u0].u.rec != nullptr;
+    size_t u1 = u0;
+    while (u1 < units.size() && u1 - u0 < size_t(kDecodeMaxUnits) && (units[u1].u.rec != nullptr) == rot) ++u1;
+    Plan p;
+    if (!plan_launch(D, ydtype, units.data() + u0, int(u1 - u0), p)) return hipErrorInvalidValue;
+    if (hipError_t e = dispatch(p, st)) return e;
+    u0 = u1;
+  }
+  return hipSuccess;
 }
 
 }  // namespace paro

@@ -33,8 +33,10 @@ paro_status check_rotation(const paro_rotation* r) {
 
 paro_status from_hip(hipError_t e) { return e == hipSuccess ? PARO_OK : PARO_EHIP; }
 
-size_t linear_ws_bytes(bool rotated, int M, int D, int N) {
-  if (!rotated || M <= 0 || fused_decode_ok(M, D, N)) return 0;
+// Workspace of one rotated call: the transformed x, unless the transform runs inside the
+// decode kernel.
+size_t rotated_ws_bytes(int K, int M, int D, int N) {
+  if (M <= 0 || N <= 0 || decode_takes(K, M, D, N)) return 0;
   return align256(size_t(M) * size_t(D) * 2);
 }
 
@@ -44,9 +46,8 @@ paro_status check_linear_args(int M, int D, int N, const void* x, const uint8_t*
   if (ydtype != PARO_F16 && ydtype != PARO_F32) return PARO_EINVAL;
   if (M == 0 || N == 0) return PARO_OK;
   if (!x || !qweight || !scales || !zeros || !y) return PARO_EINVAL;
-  if (!aligned16(x) || !aligned16(qweight) || !aligned16(y)) return PARO_EINVAL;
-  // scales/zeros rows are D/128 halves long; only 2-byte alignment is needed.
-  if ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 1u) return PARO_EINVAL;
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(y) || !aligned16(scales) || !aligned16(zeros))
+    return PARO_EINVAL;
   const size_t ybytes = size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2);
   const size_t G = size_t(D / PARO_GROUP);
   if (overlap(y, ybytes, x, size_t(M) * D * 2) || overlap(y, ybytes, qweight, size_t(N) * D / 2) ||
@@ -56,14 +57,6 @@ paro_status check_linear_args(int M, int D, int N, const void* x, const uint8_t*
 }
 
 }  // namespace
-
-bool paro::fused_decode_ok(int M, int D, int N) {
-  return M >= 1 && M <= kFusedMaxM && N >= 1 && decode_lds_bytes(true, M, D, N) <= kDecodeMaxLds;
-}
-
-bool paro::decode_ok(int M, int D, int N) {
-  return M >= 1 && M <= kDecodeMaxM && N >= 1 && decode_lds_bytes(false, M, D, N) <= kDecodeMaxLds;
-}
 
 extern "C" {
 
@@ -194,14 +187,27 @@ paro_status paro_rotate(const paro_rotation* r, int M, const void* x, void* xout
 
 size_t paro_workspace_bytes(int M, int D, int N) {
   if (M <= 0 || N < 0 || check_shape(0, D) != PARO_OK) return 0;
-  return linear_ws_bytes(true, M, D, N);
+  return align256(size_t(M) * size_t(D) * 2);  // enough for every transform (K) and path
 }
 
 static paro_status run_linear(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
                               const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, hipStream_t st) {
-  if (decode_ok(M, D, N))
-    return from_hip(launch_decode(nullptr, M, D, N, x, x_nibble_order, qweight, scales, zeros, y, ydtype, st));
+  if (decode_takes(-1, M, D, N)) {
+    const DecodeCall c{nullptr, M, N, x, x_nibble_order, qweight, scales, zeros, y};
+    return from_hip(launch_decode(D, ydtype, &c, 1, st));
+  }
   return from_hip(launch_gemm(M, D, N, x, qweight, scales, zeros, y, ydtype, st));
+}
+
+// A rotated call that the decode kernel cannot take: transform into the workspace, then the
+// linear on it (the decode kernel takes the workspace in its word order).
+static paro_status run_rotated_two_step(const DevRot& R, int M, int N, const uint16_t* x, const uint8_t* qweight,
+                                        const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype,
+                                        uint16_t* xr, hipStream_t st) {
+  const int D = R.D;
+  const bool nib = decode_takes(-1, M, D, N);
+  if (hipError_t e = launch_rotate(R, M, x, xr, nib, st)) return from_hip(e);
+  return run_linear(M, D, N, xr, nib, qweight, scales, zeros, y, ydtype, st);
 }
 
 paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t* qweight, const void* scales,
@@ -224,20 +230,120 @@ paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void
   if (M == 0 || N == 0) return PARO_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const DevRot R = dev_rot(*r);
-  if (fused_decode_ok(M, D, N))
-    return from_hip(launch_decode(&R, M, D, N, static_cast<const uint16_t*>(x), false, qweight,
-                                  static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), y,
-                                  ydtype, st));
-  const size_t need = linear_ws_bytes(true, M, D, N);
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  const uint16_t* sc = static_cast<const uint16_t*>(scales);
+  const uint16_t* zr = static_cast<const uint16_t*>(zeros);
+  if (decode_takes(R.K, M, D, N)) {
+    const DecodeCall c{&R, M, N, xh, false, qweight, sc, zr, y};
+    return from_hip(launch_decode(D, ydtype, &c, 1, st));
+  }
+  const size_t need = rotated_ws_bytes(R.K, M, D, N);
   if (!ws || ws_bytes < need) return PARO_EWORKSPACE;
   if (!aligned16(ws)) return PARO_EINVAL;
   const size_t ybytes = size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2);
   if (overlap(ws, need, x, size_t(M) * D * 2) || overlap(ws, need, y, ybytes)) return PARO_EINVAL;
-  uint16_t* xr = static_cast<uint16_t*>(ws);
-  const bool nib = decode_ok(M, D, N);  // the decode kernel takes its A operand in nibble order
-  if (hipError_t e = launch_rotate(R, M, static_cast<const uint16_t*>(x), xr, nib, st)) return from_hip(e);
-  return run_linear(M, D, N, xr, nib, qweight, static_cast<const uint16_t*>(scales),
-                    static_cast<const uint16_t*>(zeros), y, ydtype, st);
+  return run_rotated_two_step(R, M, N, xh, qweight, sc, zr, y, ydtype, static_cast<uint16_t*>(ws), st);
+}
+
+// ---- batches -------------------------------------------------------------------------------
+
+static size_t batch_ws_bytes(int count, const paro_linear_args* calls) {
+  size_t total = 0;
+  for (int i = 0; i < count; ++i)
+    if (calls[i].rot) total += rotated_ws_bytes(calls[i].rot->K, calls[i].M, calls[i].D, calls[i].N);
+  return total;
+}
+
+size_t paro_linear_batch_workspace_bytes(int count, const paro_linear_args* calls) {
+  if (count <= 0 || !calls) return 0;
+  return batch_ws_bytes(count, calls);
+}
+
+paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydtype, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (count < 0 || (count > 0 && !calls)) return PARO_EINVAL;
+  if (ydtype != PARO_F16 && ydtype != PARO_F32) return PARO_EINVAL;
+  const size_t ysz = ydtype == PARO_F32 ? 4 : 2;
+  for (int i = 0; i < count; ++i) {
+    const paro_linear_args& c = calls[i];
+    if (c.rot) {
+      if (paro_status s = check_rotation(c.rot)) return s;
+      if (c.rot->D != c.D) return PARO_EINVAL;
+    } else if (paro_status s = check_shape(0, c.D)) {
+      return s;
+    }
+    if (paro_status s = check_linear_args(c.M, c.D, c.N, c.x, c.qweight, c.scales, c.zeros, c.y, ydtype)) return s;
+  }
+  // the calls run concurrently: no call may write what another call reads or writes
+  for (int i = 0; i < count; ++i) {
+    const paro_linear_args& a = calls[i];
+    if (a.M == 0 || a.N == 0) continue;
+    const size_t ya = size_t(a.M) * size_t(a.N) * ysz;
+    for (int j = 0; j < count; ++j) {
+      const paro_linear_args& b = calls[j];
+      if (j == i || b.M == 0 || b.N == 0) continue;
+      const size_t G = size_t(b.D / PARO_GROUP);
+      if (overlap(a.y, ya, b.y, size_t(b.M) * size_t(b.N) * ysz) || overlap(a.y, ya, b.x, size_t(b.M) * b.D * 2) ||
+          overlap(a.y, ya, b.qweight, size_t(b.N) * b.D / 2) || overlap(a.y, ya, b.scales, size_t(b.N) * G * 2) ||
+          overlap(a.y, ya, b.zeros, size_t(b.N) * G * 2) ||
+          (b.rot && overlap(a.y, ya, b.rot->dev, desc_layout(b.rot->K, b.rot->D).total)))
+        return PARO_EINVAL;
+    }
+  }
+  const size_t need = batch_ws_bytes(count, calls);
+  if (need) {
+    if (!ws || ws_bytes < need) return PARO_EWORKSPACE;
+    if (!aligned16(ws)) return PARO_EINVAL;
+    for (int i = 0; i < count; ++i) {
+      const paro_linear_args& c = calls[i];
+      if (c.M == 0 || c.N == 0) continue;
+      if (overlap(ws, need, c.x, size_t(c.M) * c.D * 2) || overlap(ws, need, c.y, size_t(c.M) * size_t(c.N) * ysz))
+        return PARO_EINVAL;
+    }
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<DevRot> rots(size_t(count > 0 ? count : 0));
+  std::vector<char> done(size_t(count > 0 ? count : 0), 0);
+  // decode-shaped calls: one launch per D (transform inside the kernel where it applies)
+  for (int i = 0; i < count; ++i) {
+    if (done[i] || calls[i].M == 0 || calls[i].N == 0) {
+      done[i] = 1;
+      continue;
+    }
+    const int D = calls[i].D;
+    std::vector<DecodeCall> group;
+    for (int j = i; j < count; ++j) {
+      const paro_linear_args& c = calls[j];
+      if (done[j] || c.D != D || c.M == 0 || c.N == 0) continue;
+      if (c.rot) rots[j] = dev_rot(*c.rot);
+      if (!decode_takes(c.rot ? rots[j].K : -1, c.M, D, c.N)) continue;
+      group.push_back(DecodeCall{c.rot ? &rots[j] : nullptr, c.M, c.N, static_cast<const uint16_t*>(c.x), false,
+                                 c.qweight, static_cast<const uint16_t*>(c.scales),
+                                 static_cast<const uint16_t*>(c.zeros), c.y});
+      done[j] = 1;
+    }
+    if (!group.empty())
+      if (hipError_t e = launch_decode(D, ydtype, group.data(), int(group.size()), st)) return from_hip(e);
+  }
+  // the rest, one call at a time
+  char* wsp = static_cast<char*>(ws);
+  for (int i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    const paro_linear_args& c = calls[i];
+    const uint16_t* xh = static_cast<const uint16_t*>(c.x);
+    const uint16_t* sc = static_cast<const uint16_t*>(c.scales);
+    const uint16_t* zr = static_cast<const uint16_t*>(c.zeros);
+    paro_status s;
+    if (c.rot) {
+      const DevRot R = dev_rot(*c.rot);
+      s = run_rotated_two_step(R, c.M, c.N, xh, c.qweight, sc, zr, c.y, ydtype, reinterpret_cast<uint16_t*>(wsp), st);
+      wsp += rotated_ws_bytes(R.K, c.M, c.D, c.N);
+    } else {
+      s = run_linear(c.M, c.D, c.N, xh, false, c.qweight, sc, zr, c.y, ydtype, st);
+    }
+    if (s != PARO_OK) return s;
+  }
+  return PARO_OK;
 }
 
 }  // extern "C"

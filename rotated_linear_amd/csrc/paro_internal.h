@@ -62,31 +62,60 @@ struct StagePair {
 // and distinct second channels mod q. Returns false if D % 128 != 0 or sizes mismatch.
 bool schedule_stage(int D, std::vector<StagePair>& pairs);
 
-// Largest M the single-kernel decode path (transform fused into the decode kernel) takes.
-constexpr int kFusedMaxM = 4;
+// ---- decode-shaped linears (decode.hip) ----
 // Largest M the decode kernel takes; above it the tiled MFMA GEMM runs.
 constexpr int kDecodeMaxM = 16;
-// LDS budget of one decode workgroup.
-constexpr size_t kDecodeMaxLds = 144 * 1024;
+// Largest D for which the transform runs inside the decode kernel.
+constexpr int kDecodeFusedMaxD = 4096;
+// Threads of a decode workgroup (one workgroup per CU).
+constexpr int kDecodeThreads = 512;
+// Units (row blocks of calls) one decode launch carries in its kernel arguments.
+constexpr int kDecodeMaxUnits = 32;
 
-// Whether paro_rotated_linear runs its transform inside the decode kernel.
-bool fused_decode_ok(int M, int D, int N);
-// Whether the (plain) decode kernel takes this shape.
-bool decode_ok(int M, int D, int N);
+// One linear handed to the decode kernel. rot == nullptr: plain linear on x, whose
+// 8-channel words are in the decode order [0,4,1,5,2,6,3,7] when x_nibble_order is set.
+struct DecodeCall {
+  const DevRot* rot;
+  int M, N;
+  const uint16_t* x;
+  bool x_nibble_order;
+  const uint8_t* qweight;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  void* y;
+};
 
-// LDS bytes of a decode workgroup.
-size_t decode_lds_bytes(bool fused, int M, int D, int N);
+// Kernel argument of a decode launch: a table of units. A unit is up to 16 rows of one call
+// (up to 4 when the transform runs in the kernel); its workgroups split its 16-row weight
+// tiles, `tpb` tiles each, starting at workgroup first_block[unit].
+struct DecodeUnit {
+  const uint16_t* x;  // first row of the unit
+  const uint8_t* qw;
+  const uint16_t* sc;
+  const uint16_t* zr;
+  void* y;             // first row of the unit
+  const PairRec* rec;  // nullptr: plain
+  const float* inv_s;
+  int N, K, rows, xperm, tpb, pad;
+};
+struct DecodeArgs {
+  int D, ydtype, nunits, red_off;
+  int first_block[kDecodeMaxUnits];
+  DecodeUnit u[kDecodeMaxUnits];
+};
+
+// Whether the decode kernel takes a call of this shape: K < 0 for a plain linear, else the
+// transform's stage count (the transform then runs inside the kernel: K <= 8, D <= 4096).
+bool decode_takes(int K, int M, int D, int N);
+// Launch the decode kernel over calls that share D (several launches when the units exceed
+// one launch's table).
+hipError_t launch_decode(int D, int ydtype, const DecodeCall* calls, int count, hipStream_t st);
 
 // Kernel launchers (each returns the launch's hipError_t).
 hipError_t launch_pack(const DevRot& R, int N, const uint16_t* W, uint8_t* qweight, uint16_t* scales,
                        uint16_t* zeros, hipStream_t st);
 // nibble_order: write each 8-channel word as [0,4,1,5,2,6,3,7] (the decode kernel's A order).
 hipError_t launch_rotate(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, bool nibble_order,
-                         hipStream_t st);
-// rot == nullptr: plain linear on x (x_nibble_order tells its word order). Otherwise x is
-// transformed inside the kernel (M <= 4).
-hipError_t launch_decode(const DevRot* rot, int M, int D, int N, const uint16_t* x, bool x_nibble_order,
-                         const uint8_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype,
                          hipStream_t st);
 hipError_t launch_gemm(int M, int D, int N, const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                        const uint16_t* zeros, void* y, int ydtype, hipStream_t st);

@@ -14,7 +14,8 @@
 // clamped into range) and the stage sequence is straight-line code for K <= 8,
 // so the compiler's wait counts stay exact and a stage waits only for its own
 // records. With EXACT (the stage's pairs divide evenly over the threads) the
-// per-pair range checks disappear as well.
+// per-pair range checks disappear as well; with TIGHT (PPT == ceil(pairs / NT))
+// only the last slot of a thread can lie past the stage.
 #pragma once
 
 #include "paro_internal.h"
@@ -33,14 +34,15 @@ struct RowVec<1> {
   using T = float;
 };
 
-template <int NT, int PPT, int PD, bool EXACT>
+template <int NT, int PPT, int PD, bool EXACT, bool TIGHT = false>
 struct StageRing {
   PairRec rec[PD][PPT];
 
   // Issue the loads of stage k (clamped into [0, K)) into ring slot `slot`.
   template <int slot>
   __device__ inline void issue(int k, int K, int P, int tid, const PairRec* __restrict__ recs) {
-    const int kc = k < K ? k : K - 1;
+    int kc = k < K ? k : K - 1;
+    kc = kc > 0 ? kc : 0;  // K == 0: reads stay inside the descriptor and are never used
     const size_t base = size_t(kc) * size_t(P);
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
@@ -52,21 +54,21 @@ struct StageRing {
 
   // All of the thread's gathers first, then all updates: the pairs of a stage are disjoint,
   // but the compiler cannot know that, so interleaving reads and writes per pair would
-  // serialize every pair behind the previous pair's LDS round trip.
+  // serialize every pair behind the previous pair's LDS round trip. Gathers are unconditional
+  // (a slot past the stage holds the clamped record of pair P - 1, whose values it then
+  // ignores); updates are guarded (with TIGHT, only the last slot's).
   template <int R, int slot>
   __device__ inline void apply(typename RowVec<R>::T* rows, int P, int tid) const {
     using V = typename RowVec<R>::T;
     V vi[PPT], vj[PPT];
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
-      if (EXACT || tid + q * NT < P) {
-        vi[q] = rows[rec[slot][q].ij & 0xFFFFu];
-        vj[q] = rows[rec[slot][q].ij >> 16];
-      }
+      vi[q] = rows[rec[slot][q].ij & 0xFFFFu];
+      vj[q] = rows[rec[slot][q].ij >> 16];
     }
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
-      if (EXACT || tid + q * NT < P) {
+      if (EXACT || (TIGHT && q + 1 < PPT) || tid + q * NT < P) {
         const float c = rec[slot][q].c, s = rec[slot][q].s;
         rows[rec[slot][q].ij & 0xFFFFu] = c * vi[q] + s * vj[q];
         rows[rec[slot][q].ij >> 16] = c * vj[q] - s * vi[q];
@@ -75,17 +77,17 @@ struct StageRing {
   }
 };
 
-template <int NT, int PPT, int PD, bool EXACT, int slot = 0>
-__device__ inline void ring_prime(StageRing<NT, PPT, PD, EXACT>& ring, int K, int P, int tid,
+template <int NT, int PPT, int PD, bool EXACT, bool TIGHT, int slot = 0>
+__device__ inline void ring_prime(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, int K, int P, int tid,
                                   const PairRec* __restrict__ recs) {
   if constexpr (slot < PD) {
     ring.template issue<slot>(slot, K, P, tid, recs);
-    ring_prime<NT, PPT, PD, EXACT, slot + 1>(ring, K, P, tid, recs);
+    ring_prime<NT, PPT, PD, EXACT, TIGHT, slot + 1>(ring, K, P, tid, recs);
   }
 }
 
-template <int R, int NT, int PPT, int PD, bool EXACT, int slot = 0>
-__device__ inline void ring_round(StageRing<NT, PPT, PD, EXACT>& ring, typename RowVec<R>::T* rows, int k0, int K,
+template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT, int slot = 0>
+__device__ inline void ring_round(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, typename RowVec<R>::T* rows, int k0, int K,
                                   int P, int tid, const PairRec* __restrict__ recs) {
   if constexpr (slot < PD) {
     const int k = k0 + slot;
@@ -93,15 +95,15 @@ __device__ inline void ring_round(StageRing<NT, PPT, PD, EXACT>& ring, typename 
       ring.template apply<R, slot>(rows, P, tid);
       __syncthreads();
       ring.template issue<slot>(k + PD, K, P, tid, recs);
-      ring_round<R, NT, PPT, PD, EXACT, slot + 1>(ring, rows, k0, K, P, tid, recs);
+      ring_round<R, NT, PPT, PD, EXACT, TIGHT, slot + 1>(ring, rows, k0, K, P, tid, recs);
     }
   }
 }
 
 // Straight-line version for K <= KMAX stages: with no loop back-edge the compiler's wait
 // counts stay exact, so a stage waits only for its own records.
-template <int KMAX, int R, int NT, int PPT, int PD, bool EXACT, int k = 0>
-__device__ inline void ring_unrolled(StageRing<NT, PPT, PD, EXACT>& ring, typename RowVec<R>::T* rows, int K, int P,
+template <int KMAX, int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT, int k = 0>
+__device__ inline void ring_unrolled(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, typename RowVec<R>::T* rows, int K, int P,
                                      int tid, const PairRec* __restrict__ recs) {
   if constexpr (k < KMAX) {
     if (k < K) {  // uniform; holds no global load
@@ -109,22 +111,29 @@ __device__ inline void ring_unrolled(StageRing<NT, PPT, PD, EXACT>& ring, typena
       __syncthreads();
     }
     if constexpr (k + PD < KMAX) ring.template issue<k % PD>(k + PD, K, P, tid, recs);
-    ring_unrolled<KMAX, R, NT, PPT, PD, EXACT, k + 1>(ring, rows, K, P, tid, recs);
+    ring_unrolled<KMAX, R, NT, PPT, PD, EXACT, TIGHT, k + 1>(ring, rows, K, P, tid, recs);
   }
+}
+
+// Run K <= kUnrolledStages stages (K >= 1) as straight-line code; same contract as ring_run.
+template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT>
+__device__ inline void ring_run_short(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, float* lds, int K, int P, int tid,
+                                      const PairRec* __restrict__ recs) {
+  ring_unrolled<kUnrolledStages, R>(ring, reinterpret_cast<typename RowVec<R>::T*>(lds), K, P, tid, recs);
 }
 
 // Run all K stages (K >= 1) on the rows in LDS. The caller has issued ring_prime() early
 // (ideally before filling LDS) and must __syncthreads() between filling the rows and
 // calling this. Ends with a barrier after the last stage.
-template <int R, int NT, int PPT, int PD, bool EXACT>
-__device__ inline void ring_run(StageRing<NT, PPT, PD, EXACT>& ring, float* lds, int K, int P, int tid,
+template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT>
+__device__ inline void ring_run(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, float* lds, int K, int P, int tid,
                                 const PairRec* __restrict__ recs) {
   using V = typename RowVec<R>::T;
   V* rows = reinterpret_cast<V*>(lds);
   if (K <= kUnrolledStages) {
-    ring_unrolled<kUnrolledStages, R, NT, PPT, PD, EXACT>(ring, rows, K, P, tid, recs);
+    ring_unrolled<kUnrolledStages, R, NT, PPT, PD, EXACT, TIGHT>(ring, rows, K, P, tid, recs);
   } else {
-    for (int k0 = 0; k0 < K; k0 += PD) ring_round<R, NT, PPT, PD, EXACT>(ring, rows, k0, K, P, tid, recs);
+    for (int k0 = 0; k0 < K; k0 += PD) ring_round<R, NT, PPT, PD, EXACT, TIGHT>(ring, rows, k0, K, P, tid, recs);
   }
 }
 

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     out = subprocess.run(["nm", "-D", "--defined-only", rl.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(paro_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -50,7 +50,7 @@ def test_status_strings_and_sizes():
     assert rl.paro_rotation_bytes(0, 128) == 2 * 512
     for K, D in ((8, 100), (8, 1537), (-1, 256), (65, 256), (2, 16512), (2, 0)):
         assert rl.paro_rotation_bytes(K, D) == 0, (K, D)
-    assert rl.paro_workspace_bytes(1, 1536, 1536) == 0  # fused decode path
+    assert rl.paro_workspace_bytes(1, 1536, 1536) == 1536 * 2  # an upper bound: the fused path uses none
     assert rl.paro_workspace_bytes(64, 4096, 4096) == 64 * 4096 * 2
     assert rl.paro_workspace_bytes(0, 4096, 4096) == 0
 
@@ -151,6 +151,51 @@ def test_calls_reject_bad_arguments_before_launch():
     assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, None, 0, None) == 5
     assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, v(FAKE * 6), 100, None) == 5
     assert lib.paro_rotated_linear(None, 1, 512, *args, v(FAKE * 5), 0, None, 0, None) == 1
+
+
+def _call(rot, M, D, N, base):
+    """A batch entry with fake, non-overlapping buffers starting at FAKE * base."""
+    v = FAKE * base
+    return rl.paro_linear_args(ctypes.pointer(rot) if rot is not None else None, M, D, N, v, v + FAKE // 2,
+                               v + FAKE // 2 + FAKE // 4, v + FAKE // 2 + FAKE // 4 + FAKE // 8, v + FAKE)
+
+
+def test_batch_rejects_bad_arguments_before_launch():
+    Arr = rl.paro_linear_args * 4
+    ok = _rot(8, 256)
+    # nothing to do
+    assert lib.paro_linear_batch(0, None, 0, None, 0, None) == 0
+    assert lib.paro_linear_batch(-1, None, 0, None, 0, None) == 1
+    assert lib.paro_linear_batch(2, None, 0, None, 0, None) == 1
+    a = Arr(_call(ok, 4, 256, 64, 4), _call(None, 4, 256, 64, 8))
+    assert lib.paro_linear_batch(2, a, 7, None, 0, None) == 1  # dtype
+    a = Arr(_call(ok, 4, 512, 64, 4))  # D differs from the transform's
+    assert lib.paro_linear_batch(1, a, 0, None, 0, None) == 1
+    a = Arr(_call(None, 4, 250, 64, 4))
+    assert lib.paro_linear_batch(1, a, 0, None, 0, None) == 2
+    a = Arr(_call(_rot(8, 250), 4, 250, 64, 4))
+    assert lib.paro_linear_batch(1, a, 0, None, 0, None) == 2
+    # one call's output overlaps another call's input
+    c0, c1 = _call(ok, 4, 256, 64, 4), _call(None, 4, 256, 64, 8)
+    c1.x = c0.y
+    a = Arr(c0, c1)
+    assert lib.paro_linear_batch(2, a, 0, None, 0, None) == 1
+    c1 = _call(None, 4, 256, 64, 8)
+    c1.y = c0.y
+    a = Arr(c0, c1)
+    assert lib.paro_linear_batch(2, a, 0, None, 0, None) == 1
+    # a transform the decode kernel does not take needs a workspace
+    deep = _rot(12, 256)
+    a = Arr(_call(deep, 4, 256, 64, 4), _call(ok, 4, 256, 64, 8))
+    need = lib.paro_linear_batch_workspace_bytes(2, a)
+    assert need == 4 * 256 * 2
+    assert lib.paro_linear_batch(2, a, 0, None, 0, None) == 5
+    assert lib.paro_linear_batch(2, a, 0, ctypes.c_void_p(FAKE * 12), need - 1, None) == 5
+    assert lib.paro_linear_batch(2, a, 0, ctypes.c_void_p(FAKE * 4), need, None) == 1  # workspace overlaps x
+    big = _rot(8, 4096)
+    a = Arr(_call(big, 64, 4096, 64, 4))
+    assert lib.paro_linear_batch_workspace_bytes(1, a) == 64 * 4096 * 2
+    assert lib.paro_linear_batch_workspace_bytes(0, a) == 0
 
 
 # --------------------------------------------------------------------------- #

@@ -265,3 +265,74 @@ def test_workspace_and_determinism():
     b = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z,
                                       ws=torch.empty(need + 4096, dtype=torch.uint8, device="cuda")))
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+# --------------------------------------------------------------------------- #
+# batches: one launch for many linears, bit-identical to the single calls
+# --------------------------------------------------------------------------- #
+
+def _batch_inputs(specs):
+    """specs: (seed, M, D, N, K or None) -> list of (L, rot or None, x, packed weights on the GPU)."""
+    out = []
+    for seed, M, D, N, K in specs:
+        L = W.custom_linear(seed, M, D, N, 0 if K is None else K)
+        rot = None if K is None else _rot(L)
+        if rot is None:
+            qw, sc, z = (C.dev(t, torch) for t in O.pack_weights(L.W, L.pairs[:0], L.theta[:0], np.ones_like(L.scale)))
+        else:
+            qw, sc, z = rl.paro_pack_weights(rot, C.dev(L.W, torch))
+        out.append((L, rot, C.dev(L.x, torch), (qw, sc, z)))
+    return out
+
+
+def _single(rot, xd, w, dt):
+    if rot is None:
+        return rl.paro_w4a16_linear(xd, *w, out_dtype=dt)
+    return rl.paro_rotated_linear(rot, xd, *w, out_dtype=dt)
+
+
+@pytest.mark.parametrize("specs", [
+    # the attention projections of a decode step: q, k, v, o at M = 1, 4, 16 (D = 1536)
+    [(60 + i, M, 1536, N, 8) for M in (1, 4, 16) for i, N in enumerate((1536, 256, 256, 1536))],
+    # plain and rotated mixed, ragged N, several D, a prefill-sized call and a deep transform
+    [(70, 3, 768, 200, 8), (71, 16, 768, 77, None), (72, 5, 2048, 130, 2), (73, 1, 2048, 16, None),
+     (74, 40, 768, 96, 8), (75, 2, 768, 64, 12), (76, 7, 8960 // 70 * 70, 33, 8), (77, 1, 4096, 300, 8)],
+])
+def test_batch_matches_single_calls_bitwise(specs):
+    C.log(f"batch of {len(specs)} calls")
+    ins = _batch_inputs(specs)
+    calls = [(rot, xd, *w) for (L, rot, xd, w) in ins]
+    for dt in (torch.float32, torch.float16):
+        ys = [C.host(y) for y in rl.paro_linear_batch(calls, out_dtype=dt)]
+        for (L, rot, xd, w), y in zip(ins, ys):
+            ref = C.host(_single(rot, xd, w, dt))
+            assert np.array_equal(y.view(np.uint8), ref.view(np.uint8)), (L.spec, dt)
+    # and against the oracle (the north-star bar) for the float32 outputs
+    ys = [C.host(y) for y in rl.paro_linear_batch(calls, out_dtype=torch.float32)]
+    for (L, rot, xd, w), y in zip(ins, ys):
+        deq = O.dequantize(*(C.host(t) for t in w))
+        if rot is None:
+            ref = L.x.astype(np.float64) @ deq.T
+        else:
+            a = O.transform_activations(L.x, L.pairs, L.theta, L.scale)
+            ref = O.f16_rne(a).astype(np.float64) @ deq.T
+        mx, rel = C.linear_metrics(y, ref)
+        assert mx <= C.MAX_ABS and rel <= C.REL_L2, (L.spec, mx, rel)
+
+
+def test_batch_edge_cases():
+    C.log("batch edge cases")
+    ins = _batch_inputs([(80, 4, 256, 40, 2), (81, 1, 256, 8, None)])
+    calls = [(rot, xd, *w) for (L, rot, xd, w) in ins]
+    assert rl.paro_linear_batch([]) == []
+    # an empty call inside a batch is skipped
+    empty = (ins[0][1], torch.empty((0, 256), dtype=torch.float16, device="cuda"), *ins[0][3])
+    ys = rl.paro_linear_batch([empty] + calls, out_dtype=torch.float32)
+    assert ys[0].shape == (0, 40)
+    for (L, rot, xd, w), y in zip(ins, ys[1:]):
+        assert np.array_equal(C.host(y), C.host(_single(rot, xd, w, torch.float32)))
+    # the same batch twice: identical bits
+    a = [C.host(y) for y in rl.paro_linear_batch(calls)]
+    b = [C.host(y) for y in rl.paro_linear_batch(calls)]
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint16), v.view(np.uint16))
