@@ -40,6 +40,13 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load through a global-memory pointer.
+template <class T>
+__device__ inline uint4 ld16(gptr<const T> p) {
+  return __builtin_bit_cast(uint4, *(gptr<const u4>)p);
+}
 
 constexpr int kThreads = kDecodeThreads;
 constexpr int kWaves = kThreads / 64;
@@ -97,10 +104,10 @@ __device__ inline h8 decode_order(h8 a) { return __builtin_shufflevector(a, a, 0
 
 // The transform of a unit's rows inside the kernel: x (already in registers) -> float32 rows in
 // LDS, the K stages, then x' = rows * (1/s) as float16 chunks in the decode order.
-template <int R, int PPT, int PD>
+template <int R, int PPT, int PD, class RP>
 __device__ inline void unit_transform(StageRing<kThreads, PPT, PD, false, true>& ring, float* rot, float* isl,
                                       uint4* xs, const uint4 (&xv)[kFusedX], const float4 (&iv)[2], int rows, int D,
-                                      int K, int tid, const PairRec* __restrict__ recs) {
+                                      int K, int tid, RP recs) {
   const int chunks = D / 8, xtotal = chunks * rows;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -145,22 +152,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, h = lane >> 4;
   const int q = wave / WPT, wq = wave - q * WPT;
-  const int D = args.D, G = D / PARO_GROUP, chunks = D / 8;
-
   // ---- this workgroup's unit and tile range
+  // The unit index, then the whole unit, each in one round of scalar loads. The empty statement
+  // keeps every field in registers (else each is re-read from the kernel arguments, behind a
+  // wait, where it is used); pointers pass through it as integers and come back typed as
+  // global-memory pointers, so their loads stay global_load.
   const int b = int(blockIdx.x);
-  int ui = 0;
-#pragma unroll
-  for (int i = 1; i < kDecodeMaxUnits; ++i)
-    if (i < args.nunits && b >= int(args.first_block[i])) ui = i;
-  const DecodeUnit& U = args.u[ui];
-  const int N = U.N, rows = U.rows, K = U.K;
-  const uint8_t* __restrict__ qw = U.qw;
-  const uint32_t* __restrict__ sc32 = reinterpret_cast<const uint32_t*>(U.sc);
-  const uint32_t* __restrict__ zr32 = reinterpret_cast<const uint32_t*>(U.zr);
+  const int ui = int((reinterpret_cast<const uint32_t*>(args.unit_of_block)[b >> 2] >> ((b & 3) * 8)) & 0xFFu);
+  const DecodeUnit& Ua = args.u[ui];
+  uintptr_t ix = uintptr_t(Ua.x), iqw = uintptr_t(Ua.qw), isc = uintptr_t(Ua.sc), izr = uintptr_t(Ua.zr),
+            iy = uintptr_t(Ua.y), irec = uintptr_t(Ua.rec), iis = uintptr_t(Ua.inv_s);
+  int N = Ua.N, K = Ua.K, rows = Ua.rows, xperm = Ua.xperm, tpb = Ua.tpb, block0 = Ua.block0, D = Ua.D,
+      ydtype = Ua.ydtype, red_off = Ua.red_off;
+  asm volatile(""
+               : "+s"(ix), "+s"(iqw), "+s"(isc), "+s"(izr), "+s"(iy), "+s"(irec), "+s"(iis), "+s"(N), "+s"(K),
+                 "+s"(rows), "+s"(xperm), "+s"(tpb), "+s"(block0), "+s"(D), "+s"(ydtype), "+s"(red_off));
+  const gptr<const uint16_t> xg = (gptr<const uint16_t>)ix;
+  const gptr<const uint8_t> qw = (gptr<const uint8_t>)iqw;
+  const gptr<const uint32_t> sc32 = (gptr<const uint32_t>)isc;  // scales as aligned 32-bit words
+  const gptr<const uint32_t> zr32 = (gptr<const uint32_t>)izr;
+  const gptr<const PairRec> recs = (gptr<const PairRec>)irec;
+  const gptr<const float> inv_s = (gptr<const float>)iis;
+  const int G = D / PARO_GROUP, chunks = D / 8;
   const int tiles = (N + 15) >> 4;
-  const int t_begin = (b - int(args.first_block[ui])) * U.tpb;
-  const int my_tiles = min(U.tpb, tiles - t_begin);              // >= 1 by construction
+  const int t_begin = (b - block0) * tpb;
+  const int my_tiles = min(tpb, tiles - t_begin);                // >= 1 by construction
   const int qt = my_tiles > q ? (my_tiles - q + NQ - 1) / NQ : 0;  // tiles of this wave's stream
   const int gw = GW > 0 ? GW : (G + WPT - 1) / WPT;
   constexpr bool fused = PPT > 0;
@@ -178,19 +194,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   uint4 pv[kPlainX];
   if constexpr (fused) {
     {
-      ring_prime(ring, K, D / 2, tid, U.rec);
+      ring_prime(ring, K, D / 2, tid, recs);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         int e = tid + u * kThreads;
         e = e < D / 4 ? e : D / 4 - 1;
-        iv[u] = reinterpret_cast<const float4*>(U.inv_s)[e];
+        iv[u] = __builtin_bit_cast(float4, ld16(inv_s + size_t(e) * 4));
       }
 #pragma unroll
       for (int u = 0; u < kFusedX; ++u) {
         int e = tid + u * kThreads;
         e = e < xtotal ? e : xtotal - 1;
         const int m = e / chunks, c = e - m * chunks;
-        xv[u] = *reinterpret_cast<const uint4*>(U.x + size_t(m) * D + size_t(c) * 8);
+        xv[u] = ld16(xg + size_t(m) * D + size_t(c) * 8);
       }
     }
   }
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
         int e = tid + u * kThreads;  // LDS chunk e = c * rows + m
         e = e < xtotal ? e : xtotal - 1;
         const int c = e / rows, m = e - c * rows;
-        pv[u] = *reinterpret_cast<const uint4*>(U.x + size_t(m) * D + size_t(c) * 8);
+        pv[u] = ld16(xg + size_t(m) * D + size_t(c) * 8);
       }
     }
   }
@@ -220,8 +236,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
     int n = row0 + j * (NQ * 16);
     n = n < N ? n : N - 1;
     g = g < G ? g : G - 1;
-    w = *reinterpret_cast<const uint4*>(qw + (uint32_t(n) * rowb + uint32_t(g) * 64u + uint32_t(h) * 16u));
-    const uint32_t gi = uint32_t(n) * uint32_t(G) + uint32_t(g);
+    w = ld16(qw + (__umul24(uint32_t(n), rowb) + uint32_t(g) * 64u + uint32_t(h) * 16u));
+    const uint32_t gi = __umul24(uint32_t(n), uint32_t(G)) + uint32_t(g);
     sw = sc32[gi >> 1];
     zw = zr32[gi >> 1];
   };
@@ -255,15 +271,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
       float* isl = reinterpret_cast<float*>(smem + L.isv);
       const int R = rows_class(rows);
       if (R == 1)
-        unit_transform<1>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, U.rec);
+        unit_transform<1>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, recs);
       else if (R == 2)
-        unit_transform<2>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, U.rec);
+        unit_transform<2>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, recs);
       else
-        unit_transform<4>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, U.rec);
+        unit_transform<4>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, recs);
     }
   }
   if constexpr (!fused) {
-    const bool perm = !U.xperm;
+    const bool perm = !xperm;
 #pragma unroll
     for (int u = 0; u < kPlainX; ++u) {
       const int e = tid + u * kThreads;
@@ -275,6 +291,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   }
   __syncthreads();
 
+  // A chunk of group g, MFMA kk, for this lane: xs[(16 g + kk) * rows + lane_off], lane_off =
+  // 4 h rows + nl (the group part is uniform; 24-bit products keep the index math 32-bit)
+  const int lane_off = int(__umul24(uint32_t(4 * h), uint32_t(rows))) + nl;
+  const bool lane_row = nl < rows;
   h8 areg[GW > 0 ? GW : 1][4];
   if constexpr (GW > 0) {
 #pragma unroll
@@ -282,14 +302,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
       const int g = wq + WPT * i;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int idx = (nl < rows && g < G) ? (g * 16 + 4 * h + kk) * rows + nl : zero_idx;
+        const int idx = (lane_row && g < G) ? (g * 16 + kk) * rows + lane_off : zero_idx;
         areg[i][kk] = __builtin_bit_cast(h8, xs[idx]);
       }
     }
   }
 
   // ---- stream the weights
-  f4* red = reinterpret_cast<f4*>(smem + args.red_off);  // [tile][WPT][RL] partial sums
+  f4* red = reinterpret_cast<f4*>(smem + red_off);  // [tile][WPT][RL] partial sums
   const int RL = 16 * ((rows + 3) >> 2);                 // lanes holding rows < `rows`
   const uint32_t km0 = 0x000F000Fu, km1 = 0x00F000F0u, ke = 0x64006400u;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -297,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   auto mac = [&](int j, int g, const h8(&a)[4], const uint4& w, uint32_t sw, uint32_t zw) {
     int n = row0 + j * (NQ * 16);
     n = n < N ? n : N - 1;
-    const bool hi = ((uint32_t(n) * uint32_t(G) + uint32_t(g)) & 1u) != 0;
+    const bool hi = (((n & G) ^ g) & 1) != 0;  // parity of n * G + g: which half of the word
     const _Float16 z = __builtin_bit_cast(_Float16, uint16_t(hi ? zw >> 16 : zw));
     const _Float16 sc = __builtin_bit_cast(_Float16, uint16_t(hi ? sw >> 16 : sw));
     const _Float16 zl = -(static_cast<_Float16>(1024.0f) + z), zh = -(static_cast<_Float16>(64.0f) + z);
@@ -344,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
           h8 a[4];
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            a[kk] = __builtin_bit_cast(h8, xs[nl < rows ? (g * 16 + 4 * h + kk) * rows + nl : zero_idx]);
+            a[kk] = __builtin_bit_cast(h8, xs[lane_row ? (g * 16 + kk) * rows + lane_off : zero_idx]);
           mac(cj, g, a, wr[s], sr[s], zr[s]);
         }
         if (cg == gw - 1) park(cj);
@@ -381,10 +401,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
     for (int w = 0; w < WPT; ++w) v += red[(tl * WPT + w) * RL + ln][m & 3];
     const int n = (t_begin + tl) * 16 + c;
     if (n < N) {
-      if (args.ydtype == PARO_F32)
-        static_cast<float*>(U.y)[size_t(m) * N + n] = v;
+      if (ydtype == PARO_F32)
+        ((gptr<float>)iy)[size_t(m) * N + n] = v;
       else
-        static_cast<_Float16*>(U.y)[size_t(m) * N + n] = static_cast<_Float16>(v);
+        ((gptr<_Float16>)iy)[size_t(m) * N + n] = static_cast<_Float16>(v);
     }
   }
 }
@@ -483,9 +503,6 @@ bool plan_launch(int D, int ydtype, const UnitSrc* units, int n, Plan& p) {
   long budget = kCUs;  // workgroups to spread; grows only if the LDS does not fit
   for (;;) {
     memset(&p.args, 0, sizeof(p.args));
-    p.args.D = D;
-    p.args.ydtype = ydtype;
-    p.args.nunits = n;
     long grid = 0;
     size_t xs_end = 0, red = 0;
     for (int i = 0; i < n; ++i) {
@@ -496,18 +513,23 @@ bool plan_launch(int D, int ydtype, const UnitSrc* units, int n, Plan& p) {
       nb = (t + tpb - 1) / tpb;
       p.args.u[i] = units[i].u;
       p.args.u[i].tpb = tpb;
-      p.args.first_block[i] = int(grid);
+      p.args.u[i].block0 = int(grid);
+      for (long k = grid; k < grid + nb && k < kDecodeMaxBlocks; ++k) p.args.unit_of_block[k] = (unsigned char)i;
       grid += nb;
       const UnitLds L = UnitLds::make(units[i].u.rec != nullptr, units[i].u.rows, D);
       xs_end = L.end > xs_end ? L.end : xs_end;
       const size_t r = size_t(tpb) * p.wpt * (16 * ((units[i].u.rows + 3) / 4)) * 16;
       red = r > red ? r : red;
     }
-    p.args.red_off = int(align1k(xs_end));
+    for (int i = 0; i < n; ++i) {
+      p.args.u[i].D = D;
+      p.args.u[i].ydtype = ydtype;
+      p.args.u[i].red_off = int(align1k(xs_end));
+    }
     p.lds = align1k(xs_end) + red;
     p.grid = int(grid);
-    if (p.lds <= kLdsLimit && grid <= 65535) return true;
-    if (budget >= total || grid > 65535) return false;
+    if (p.lds <= kLdsLimit && grid <= kDecodeMaxBlocks) return true;
+    if (budget >= total || grid > kDecodeMaxBlocks) return false;
     budget *= 2;  // more workgroups, fewer tiles each
   }
 }
@@ -516,6 +538,8 @@ bool plan_launch(int D, int ydtype, const UnitSrc* units, int n, Plan& p) {
 
 bool decode_takes(int K, int M, int D, int N) {
   if (M < 1 || M > kDecodeMaxM || N < 1 || D < PARO_GROUP || D > PARO_MAX_D || D % PARO_GROUP) return false;
+  // 24-bit row products and 32-bit byte offsets into the packed weights
+  if (N >= (1 << 24) || size_t(N) * size_t(D / 2) >= (size_t(1) << 31)) return false;
   return K < 0 || (D <= kDecodeFusedMaxD && K <= kUnrolledStages);
 }
 

@@ -69,8 +69,9 @@ constexpr int kDecodeMaxM = 16;
 constexpr int kDecodeFusedMaxD = 4096;
 // Threads of a decode workgroup (one workgroup per CU).
 constexpr int kDecodeThreads = 512;
-// Units (row blocks of calls) one decode launch carries in its kernel arguments.
+// Units (row blocks of calls) and workgroups one decode launch carries in its kernel arguments.
 constexpr int kDecodeMaxUnits = 32;
+constexpr int kDecodeMaxBlocks = 1024;
 
 // One linear handed to the decode kernel. rot == nullptr: plain linear on x, whose
 // 8-channel words are in the decode order [0,4,1,5,2,6,3,7] when x_nibble_order is set.
@@ -87,7 +88,8 @@ struct DecodeCall {
 
 // Kernel argument of a decode launch: a table of units. A unit is up to 16 rows of one call
 // (up to 4 when the transform runs in the kernel); its workgroups split its 16-row weight
-// tiles, `tpb` tiles each, starting at workgroup first_block[unit].
+// tiles, `tpb` tiles each, starting at workgroup block0. unit_of_block maps a workgroup to its
+// unit, so a workgroup reads its unit after one dependent load.
 struct DecodeUnit {
   const uint16_t* x;  // first row of the unit
   const uint8_t* qw;
@@ -96,12 +98,12 @@ struct DecodeUnit {
   void* y;             // first row of the unit
   const PairRec* rec;  // nullptr: plain
   const float* inv_s;
-  int N, K, rows, xperm, tpb, pad;
+  int N, K, rows, xperm, tpb, block0;
+  int D, ydtype, red_off, pad;  // the same for every unit of a launch
 };
 struct DecodeArgs {
-  int D, ydtype, nunits, red_off;
-  int first_block[kDecodeMaxUnits];
   DecodeUnit u[kDecodeMaxUnits];
+  unsigned char unit_of_block[kDecodeMaxBlocks];
 };
 
 // Whether the decode kernel takes a call of this shape: K < 0 for a plain linear, else the

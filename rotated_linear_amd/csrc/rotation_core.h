@@ -39,8 +39,8 @@ struct StageRing {
   PairRec rec[PD][PPT];
 
   // Issue the loads of stage k (clamped into [0, K)) into ring slot `slot`.
-  template <int slot>
-  __device__ inline void issue(int k, int K, int P, int tid, const PairRec* __restrict__ recs) {
+  template <int slot, class RP>
+  __device__ inline void issue(int k, int K, int P, int tid, RP recs) {
     int kc = k < K ? k : K - 1;
     kc = kc > 0 ? kc : 0;  // K == 0: reads stay inside the descriptor and are never used
     const size_t base = size_t(kc) * size_t(P);
@@ -48,7 +48,10 @@ struct StageRing {
     for (int q = 0; q < PPT; ++q) {
       int p = tid + q * NT;
       if constexpr (!EXACT) p = p < P ? p : P - 1;
-      rec[slot][q] = recs[base + p];
+      const auto& r = recs[base + p];  // field by field: recs may be a global-address-space pointer
+      rec[slot][q].ij = r.ij;
+      rec[slot][q].c = r.c;
+      rec[slot][q].s = r.s;
     }
   }
 
@@ -77,57 +80,56 @@ struct StageRing {
   }
 };
 
-template <int NT, int PPT, int PD, bool EXACT, bool TIGHT, int slot = 0>
-__device__ inline void ring_prime(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, int K, int P, int tid,
-                                  const PairRec* __restrict__ recs) {
+template <int NT, int PPT, int PD, bool EXACT, bool TIGHT, int slot = 0, class RP>
+__device__ inline void ring_prime(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, int K, int P, int tid, RP recs) {
   if constexpr (slot < PD) {
     ring.template issue<slot>(slot, K, P, tid, recs);
-    ring_prime<NT, PPT, PD, EXACT, TIGHT, slot + 1>(ring, K, P, tid, recs);
+    ring_prime<NT, PPT, PD, EXACT, TIGHT, slot + 1, RP>(ring, K, P, tid, recs);
   }
 }
 
-template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT, int slot = 0>
+template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT, int slot = 0, class RP>
 __device__ inline void ring_round(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, typename RowVec<R>::T* rows, int k0, int K,
-                                  int P, int tid, const PairRec* __restrict__ recs) {
+                                  int P, int tid, RP recs) {
   if constexpr (slot < PD) {
     const int k = k0 + slot;
     if (k < K) {
       ring.template apply<R, slot>(rows, P, tid);
       __syncthreads();
       ring.template issue<slot>(k + PD, K, P, tid, recs);
-      ring_round<R, NT, PPT, PD, EXACT, TIGHT, slot + 1>(ring, rows, k0, K, P, tid, recs);
+      ring_round<R, NT, PPT, PD, EXACT, TIGHT, slot + 1, RP>(ring, rows, k0, K, P, tid, recs);
     }
   }
 }
 
 // Straight-line version for K <= KMAX stages: with no loop back-edge the compiler's wait
 // counts stay exact, so a stage waits only for its own records.
-template <int KMAX, int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT, int k = 0>
+template <int KMAX, int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT, int k = 0, class RP>
 __device__ inline void ring_unrolled(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, typename RowVec<R>::T* rows, int K, int P,
-                                     int tid, const PairRec* __restrict__ recs) {
+                                     int tid, RP recs) {
   if constexpr (k < KMAX) {
     if (k < K) {  // uniform; holds no global load
       ring.template apply<R, k % PD>(rows, P, tid);
       __syncthreads();
     }
     if constexpr (k + PD < KMAX) ring.template issue<k % PD>(k + PD, K, P, tid, recs);
-    ring_unrolled<KMAX, R, NT, PPT, PD, EXACT, TIGHT, k + 1>(ring, rows, K, P, tid, recs);
+    ring_unrolled<KMAX, R, NT, PPT, PD, EXACT, TIGHT, k + 1, RP>(ring, rows, K, P, tid, recs);
   }
 }
 
 // Run K <= kUnrolledStages stages (K >= 1) as straight-line code; same contract as ring_run.
-template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT>
+template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT, class RP>
 __device__ inline void ring_run_short(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, float* lds, int K, int P, int tid,
-                                      const PairRec* __restrict__ recs) {
+                                      RP recs) {
   ring_unrolled<kUnrolledStages, R>(ring, reinterpret_cast<typename RowVec<R>::T*>(lds), K, P, tid, recs);
 }
 
 // Run all K stages (K >= 1) on the rows in LDS. The caller has issued ring_prime() early
 // (ideally before filling LDS) and must __syncthreads() between filling the rows and
 // calling this. Ends with a barrier after the last stage.
-template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT>
+template <int R, int NT, int PPT, int PD, bool EXACT, bool TIGHT, class RP>
 __device__ inline void ring_run(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, float* lds, int K, int P, int tid,
-                                const PairRec* __restrict__ recs) {
+                                RP recs) {
   using V = typename RowVec<R>::T;
   V* rows = reinterpret_cast<V*>(lds);
   if (K <= kUnrolledStages) {
@@ -136,6 +138,10 @@ __device__ inline void ring_run(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, floa
     for (int k0 = 0; k0 < K; k0 += PD) ring_round<R, NT, PPT, PD, EXACT, TIGHT>(ring, rows, k0, K, P, tid, recs);
   }
 }
+
+// A pointer into global memory whose address space the compiler knows (its loads are global_load).
+template <class T>
+using gptr = __attribute__((address_space(1))) T*;
 
 // Slot of channel offset e (0..7) of an 8-channel word in the order the INT4
 // decode produces: [0, 4, 1, 5, 2, 6, 3, 7].
