@@ -277,6 +277,9 @@ def paro_w4a16_linear(x, qweight, scales, zeros, out_dtype=None, out=None, ws=No
     _want(scales, torch.float16, (N, D // GROUP), "scales")
     _want(zeros, torch.float16, (N, D // GROUP), "zeros")
     y = _linear_out(M, N, out_dtype or torch.float16, x.device, out)
+    need = _lib.paro_workspace_bytes(M, D, N)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
         _check(_lib.paro_w4a16_linear(M, D, N, _ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), _ydt(y),
                                       _ptr(ws), ws.numel() if ws is not None else 0, _stream_ptr(x.device)),

@@ -25,7 +25,8 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 # per-file extras: the build-time pack must round every float64 product and sum on its own
-EXTRA = {"pack.hip": ["-ffp-contract=off"]}
+# the GEMM keeps its accumulators in architectural registers (the per-group rescale multiplies them)
+EXTRA = {"pack.hip": ["-ffp-contract=off"], "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 SOURCES = ["paro_api.cpp", "schedule.cpp", "pack.hip", "rotate.hip", "decode.hip", "gemm.hip"]
 
 

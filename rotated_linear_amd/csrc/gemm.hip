@@ -5,20 +5,35 @@
 // deployment", section "From fake quantization to a real TensorRT engine";
 // group size 128, section "My reduced-calibration experiment").
 //
-// Design:
-//   * the K loop walks one 128-channel quantization group at a time;
-//   * the group's A tile (x or the transformed x, float16) and the group's
-//     dequantized B tile are staged in LDS. B holds the exact integers (q - z)
-//     as float16 (nibble -> 1024 + q by an AND-OR with the 0x6400 exponent
-//     pattern, minus 1024 + z, both exact), so v_mfma_f32_16x16x32_f16 forms
-//     exact products summed in float32;
-//   * the per-(n, group) scale is applied in float32 after the group's MFMAs
-//     (acc += scale * acc_group), never folded into float16 weights;
-//   * the AND-OR decode of a 32-bit word yields channels in the order
-//     [0,4,1,5,2,6,3,7]; the A tile is written to LDS with every 8-channel
-//     word permuted the same way, so A and B agree on the reduction order;
-//   * the next group's global loads are issued before the current group's
-//     MFMAs (register double buffering).
+// Design for gfx950 (4 waves per workgroup; a pipeline stage is half a 128-channel group):
+//   * v_mfma_f32_32x32x16_f16. The workgroup tile is BM x BN, its 2 x 2 waves each own a
+//     (BM/2) x (BN/2) block of 32 x 32 accumulator tiles, held in architectural registers so
+//     the per-group rescale below is one multiply per accumulator;
+//   * a stage's A tile (x or the transformed x, float16) is staged through registers into
+//     LDS (rows padded to 144 bytes: the MFMA fragment reads are conflict-free). Its B tile
+//     stays PACKED in LDS (32 bytes per weight row, padded to 48) and every wave decodes its
+//     fragments in registers: (u & 0x000F000F) | 0x64006400 is float16 1024 + q, the nibbles
+//     at bits 4..7 give 1024 + 16 q (brought back with one fused multiply-add by 1/16), and
+//     subtracting 1024 + z leaves the exact integer q - z. Keeping B packed makes its LDS
+//     traffic a quarter of a float16 tile's;
+//   * lane half h of MFMA step kk uses the stage's 8-channel chunk 4 h + kk, so a lane's B
+//     words for a stage are 16 contiguous bytes (one LDS read) and its A chunks 64 contiguous
+//     bytes. The decode order of a word is [0,4,1,5,2,6,3,7]; A is written to LDS in that
+//     order (or arrives in it from the transform kernel);
+//   * the group scale is applied in float32 without a second accumulator: before group g's
+//     MFMAs every accumulator is multiplied by s[n][g-1] / s[n][g] (float32), and after the
+//     last group by s[n][g_last]. The products (q - z) x are exact, and the dequantized
+//     weights are never rounded;
+//   * two stages of global loads are in flight in registers while a stage computes, with a
+//     double-buffered LDS tile and one barrier per stage; the loads use 32-bit byte offsets
+//     from the operands' base addresses;
+//   * workgroup -> tile: consecutive workgroups go to different XCDs (8 on MI355X), so each
+//     XCD is given a contiguous range of tile indices and tiles are numbered in column
+//     groups of kGroupM tile rows: an XCD's tiles share A rows and weight rows in its L2;
+//   * optional split-K: split s of S takes a contiguous range of groups and writes float32
+//     partial sums; a second kernel adds the S partials in order (deterministic).
+#include <algorithm>
+
 #include "paro_internal.h"
 
 namespace paro {
@@ -26,191 +41,423 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16x __attribute__((ext_vector_type(16)));
 
-constexpr int BK = PARO_GROUP;   // one group per K step
-constexpr int LDA = BK + 8;      // LDS row stride in halves (16-byte pad)
+constexpr int kThreads = 256;
+constexpr int kBK = 64;      // channels per pipeline stage (half a quantization group)
+constexpr int kLdaH = 72;    // float16 elements per A row in LDS (64 + 8 pad: conflict-free reads)
+constexpr int kLdbB = 48;    // bytes per packed B row in LDS (32 + 16 pad)
+constexpr int kGroupM = 4;   // tile rows per column group of the tile order
+constexpr int kXcds = 8;
 
-__device__ inline uint32_t dq2(uint32_t u, uint32_t zz) {
-  // (1024 + q) - (1024 + z) for the two nibbles selected by 0x000F000F
-  const h2 v = __builtin_bit_cast(h2, (u & 0x000F000Fu) | 0x64006400u) - __builtin_bit_cast(h2, zz);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-template <int BM, int BN, int WM, int WN>
-struct Cfg {
-  static constexpr int kWaves = WM * WN;
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int TM = BM / WM / 16;  // 16x16 tiles per wave along M
-  static constexpr int TN = BN / WN / 16;  // along N
-  static constexpr int A_VEC = BM * BK / 8 / kThreads;  // 16-byte A loads per thread per group
-  static constexpr int B_VEC = BN * BK / 32 / kThreads;  // 16-byte qweight loads per thread per group
-  static constexpr size_t kLds = size_t(BM + BN) * LDA * 2 + BN * 4;
-  static_assert(BM * BK / 8 % kThreads == 0, "A tile split");
-  static_assert(BN * BK / 32 % kThreads == 0 || B_VEC == 0, "B tile split");
+// BM x BN workgroup tile; its 4 waves form WM rows x (4 / WM) columns.
+template <int BM, int BN, int WM>
+struct Tile {
+  static constexpr int WN = 4 / WM;
+  static constexpr int TM = BM / WM / 32;  // 32-row accumulator tiles per wave
+  static constexpr int TN = BN / WN / 32;  // 32-column accumulator tiles per wave
+  static constexpr int A_LD = BM * 8 / kThreads;                   // 16-byte A chunks per thread per stage
+  static constexpr int B_LD = (BN * 2 + kThreads - 1) / kThreads;  // 16-byte B chunks per thread per stage
+  static constexpr size_t A_BYTES = size_t(BM) * kLdaH * 2;
+  static constexpr size_t B_BYTES = size_t(BN) * kLdbB;
+  static constexpr size_t Z_BYTES = size_t(BN) * 8;  // two float16 pairs per column
+  static constexpr size_t R_BYTES = size_t(BN) * 4;  // float32 ratio per column
+  static constexpr size_t BUF = A_BYTES + B_BYTES + Z_BYTES + R_BYTES;
+  static constexpr size_t LDS = 2 * BUF;
+  static_assert(TM * WM * 32 == BM && TN * WN * 32 == BN && BN <= kThreads, "tile shape");
+  static_assert(BM * 8 % kThreads == 0, "A chunks per thread");
 };
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
-    int M, int D, int N, const uint16_t* __restrict__ x, const uint8_t* __restrict__ qweight,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, void* __restrict__ y, int ydtype) {
-  using C = Cfg<BM, BN, WM, WN>;
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
+
+// 8 nibbles of one 32-bit word -> exact (q - z) as float16 in the order [0,4,1,5,2,6,3,7].
+// zlo = -(1024 + z) and zhi = -(64 + z) as float16 pairs.
+__device__ inline h8 dequant_word(uint32_t u, h2 zlo, h2 zhi) {
+  const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, e = 0x64006400u;
+  const h2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const uint32_t v = u >> 8;
+  const h2 a0 = __builtin_bit_cast(h2, and_or(u, m0, e)) + zlo;
+  const h2 a1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(u, m1, e)), sixteenth, zhi);
+  const h2 a2 = __builtin_bit_cast(h2, and_or(v, m0, e)) + zlo;
+  const h2 a3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(v, m1, e)), sixteenth, zhi);
+  const uint4 o = {__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                   __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)};
+  return __builtin_bit_cast(h8, o);
+}
+
+template <class T>
+using gptr = __attribute__((address_space(1))) T*;
+
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+template <class T>
+__device__ inline uint4 ld16(const T* base, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, *reinterpret_cast<gptr<const u4>>(reinterpret_cast<uintptr_t>(base) + byte_off));
+}
+
+struct GemmArgs {
+  const uint16_t* x;
+  const uint8_t* qw;
+  const uint16_t* sc;
+  const uint16_t* zr;
+  void* y;
+  float* part;  // split-K partial sums [S][M][N] (S > 1)
+  int M, D, N, G;
+  int tiles_m, tiles_n, splits, gps;  // gps: groups per split
+  int ydtype, ldy;                    // ldy: row stride of y in elements (partials use N)
+};
+
+// Global loads of one stage (half a group): A chunks, packed B chunks, the column's scale and zero.
+template <class T>
+struct Stage {
+  uint4 a[T::A_LD];
+  uint4 b[T::B_LD];
+  uint32_t s, z;
+};
+
+template <int BM, int BN, int WM, int PD, bool APERM>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs p) {
+  using T = Tile<BM, BN, WM>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  _Float16* As = reinterpret_cast<_Float16*>(smem);  // [BM][LDA]
-  _Float16* Bs = As + BM * LDA;                       // [BN][LDA]
-  float* Ss = reinterpret_cast<float*>(Bs + BN * LDA);  // [BN]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / T::WN, wn = wave - wm * T::WN;
+  const int M = p.M, D = p.D, N = p.N, G = p.G;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int G = D / BK;
+  // ---- workgroup -> (split, tile): XCD ranges, then column groups of kGroupM tile rows
+  const int W = p.tiles_m * p.tiles_n * p.splits;
+  const int b = blockIdx.x, xcd = b % kXcds;
+  const int w = xcd * (W / kXcds) + min(xcd, W % kXcds) + b / kXcds;
+  const int T_ = p.tiles_m * p.tiles_n;
+  const int split = w / T_, t = w - split * T_;
+  const int per_group = kGroupM * p.tiles_n;
+  const int cg = t / per_group, in = t - cg * per_group;
+  const int rows_here = min(kGroupM, p.tiles_m - cg * kGroupM);
+  const int tm = cg * kGroupM + in % rows_here, tn = in / rows_here;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int g_begin = split * p.gps;
+  const int g_end = min(G, g_begin + p.gps);
+  const int ns = 2 * (g_end - g_begin);  // stages; >= 2 by construction
 
-  // per-thread staging registers
-  uint4 areg[C::A_VEC];
-  uint4 breg[C::B_VEC > 0 ? C::B_VEC : 1];
-  uint32_t zreg[C::B_VEC > 0 ? C::B_VEC : 1];
-  float sreg[C::B_VEC > 0 ? C::B_VEC : 1];
-
-  auto load_group = [&](int g) {
+  // ---- global load addressing: 32-bit byte offsets from the operands' bases (rows past M / N
+  // repeat the last row; their results are never stored)
+  uint32_t a_off[T::A_LD];
 #pragma unroll
-    for (int i = 0; i < C::A_VEC; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int r = idx / (BK / 8), w = idx % (BK / 8);
-      const int m = m0 + r;
-      areg[i] = m < M ? *reinterpret_cast<const uint4*>(x + size_t(m) * D + size_t(g) * BK + w * 8)
-                      : make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < T::A_LD; ++i) {
+    const int e = tid + i * kThreads, r = e >> 3, c = e & 7;
+    a_off[i] = uint32_t(min(m0 + r, M - 1)) * uint32_t(D) * 2u + uint32_t(c) * 16u;
+  }
+  uint32_t b_off[T::B_LD];
+#pragma unroll
+  for (int i = 0; i < T::B_LD; ++i) {
+    const int e = min(tid + i * kThreads, BN * 2 - 1), r = e >> 1, c = e & 1;
+    b_off[i] = uint32_t(min(n0 + r, N - 1)) * uint32_t(D / 2) + uint32_t(c) * 16u;
+  }
+  const uint32_t sz_off = uint32_t(min(n0 + min(tid, BN - 1), N - 1)) * uint32_t(G) * 2u;
+
+  auto load = [&](Stage<T>& s, int j) {
+    j = min(j, ns - 1);  // past the range: reload the last stage (unused)
+    const int g = g_begin + (j >> 1), half = j & 1;
+    const uint32_t ka = uint32_t(g) * 256u + uint32_t(half) * 128u;  // A bytes into the row
+    const uint32_t kb = uint32_t(g) * 64u + uint32_t(half) * 32u;    // packed B bytes into the row
+#pragma unroll
+    for (int i = 0; i < T::A_LD; ++i) s.a[i] = ld16(p.x, a_off[i] + ka);
+#pragma unroll
+    for (int i = 0; i < T::B_LD; ++i) s.b[i] = ld16(p.qw, b_off[i] + kb);
+    s.s = *reinterpret_cast<gptr<const uint16_t>>(reinterpret_cast<uintptr_t>(p.sc) + sz_off + uint32_t(g) * 2u);
+    s.z = *reinterpret_cast<gptr<const uint16_t>>(reinterpret_cast<uintptr_t>(p.zr) + sz_off + uint32_t(g) * 2u);
+  };
+
+  float prev_s = 1.f;  // the scale of the previous group of this column (threads < BN)
+  auto store = [&](const Stage<T>& s, int buf, int j) {
+    unsigned char* base = smem + buf * T::BUF;
+    _Float16* As = reinterpret_cast<_Float16*>(base);
+    unsigned char* Bs = base + T::A_BYTES;
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(base + T::A_BYTES + T::B_BYTES);
+    float* Rs = reinterpret_cast<float*>(base + T::A_BYTES + T::B_BYTES + T::Z_BYTES);
+#pragma unroll
+    for (int i = 0; i < T::A_LD; ++i) {
+      const int e = tid + i * kThreads, r = e >> 3, c = e & 7;
+      h8 v = __builtin_bit_cast(h8, s.a[i]);
+      if constexpr (!APERM) v = __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7);
+      *reinterpret_cast<h8*>(As + r * kLdaH + c * 8) = v;
     }
 #pragma unroll
-    for (int i = 0; i < C::B_VEC; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int r = idx / (BK / 32), w = idx % (BK / 32);
-      const int n = n0 + r;
-      if (n < N) {
-        breg[i] = *reinterpret_cast<const uint4*>(qweight + size_t(n) * (D / 2) + size_t(g) * (BK / 2) + w * 16);
-        const _Float16 z = __builtin_bit_cast(_Float16, zeros[size_t(n) * G + g]);
-        const _Float16 zz = static_cast<_Float16>(1024.0f) + z;
-        zreg[i] = uint32_t(__builtin_bit_cast(uint16_t, zz)) * 0x10001u;
-        sreg[i] = static_cast<float>(__builtin_bit_cast(_Float16, scales[size_t(n) * G + g]));
-      } else {
-        breg[i] = make_uint4(0u, 0u, 0u, 0u);
-        zreg[i] = 0x64006400u;
-        sreg[i] = 0.f;
+    for (int i = 0; i < T::B_LD; ++i) {
+      const int e = tid + i * kThreads;
+      if (T::B_LD * kThreads == BN * 2 || e < BN * 2)
+        *reinterpret_cast<uint4*>(Bs + (e >> 1) * kLdbB + (e & 1) * 16) = s.b[i];
+    }
+    if (tid < BN) {
+      if ((j & 1) == 0) {  // a group's first stage: the ratio to the previous group's scale
+        const float cur = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(s.s)));
+        Rs[tid] = j == 0 ? 1.f : prev_s / cur;
+        prev_s = cur;
+      }
+      const _Float16 z = __builtin_bit_cast(_Float16, uint16_t(s.z));
+      const _Float16 zl = -(static_cast<_Float16>(1024.0f) + z), zh = -(static_cast<_Float16>(64.0f) + z);
+      const h2 zl2 = {zl, zl}, zh2 = {zh, zh};
+      Zs[2 * tid] = __builtin_bit_cast(uint32_t, zl2);
+      Zs[2 * tid + 1] = __builtin_bit_cast(uint32_t, zh2);
+    }
+  };
+
+  f16x acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int l32 = lane & 31, hh = lane >> 5;
+  // one stage: lane half hh of MFMA step kk uses the stage's 8-channel chunk 4 hh + kk
+  auto compute = [&](int buf, bool group_start) {
+    const unsigned char* base = smem + buf * T::BUF;
+    const _Float16* As = reinterpret_cast<const _Float16*>(base);
+    const unsigned char* Bs = base + T::A_BYTES;
+    const uint32_t* Zs = reinterpret_cast<const uint32_t*>(base + T::A_BYTES + T::B_BYTES);
+    const float* Rs = reinterpret_cast<const float*>(base + T::A_BYTES + T::B_BYTES + T::Z_BYTES);
+    uint4 bw[T::TN];
+    h2 zl[T::TN], zh[T::TN];
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const int n = wn * (BN / T::WN) + j * 32 + l32;
+      bw[j] = *reinterpret_cast<const uint4*>(Bs + n * kLdbB + hh * 16);
+      zl[j] = __builtin_bit_cast(h2, Zs[2 * n]);
+      zh[j] = __builtin_bit_cast(h2, Zs[2 * n + 1]);
+    }
+    if (group_start) {
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        const float r = Rs[wn * (BN / T::WN) + j * 32 + l32];
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) acc[i][j] *= r;
+      }
+    }
+    const _Float16* arow = As + (wm * (BM / WM) + l32) * kLdaH + hh * 32;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      h8 af[T::TM];
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i) af[i] = *reinterpret_cast<const h8*>(arow + i * 32 * kLdaH + kk * 8);
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        const uint32_t u = kk == 0 ? bw[j].x : kk == 1 ? bw[j].y : kk == 2 ? bw[j].z : bw[j].w;
+        const h8 bf = dequant_word(u, zl[j], zh[j]);
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][j], 0, 0, 0);
       }
     }
   };
 
-  auto store_group = [&]() {
+  // ---- main loop: PD register stages of global loads in flight, double-buffered LDS, one
+  // barrier per stage. Step t computes stage t from LDS buffer t % 2 after issuing the loads of
+  // stage t + PD into the register stage that held stage t, then moves stage t + 1 from its
+  // registers into the other buffer: a load has PD stage computations to arrive.
+  constexpr int U = PD == 3 ? 6 : 2;  // steps per loop iteration: static register/buffer indices
+  Stage<T> reg[PD];
 #pragma unroll
-    for (int i = 0; i < C::A_VEC; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int r = idx / (BK / 8), w = idx % (BK / 8);
-      const h8 v = __builtin_bit_cast(h8, areg[i]);
-      const h8 p = __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7);
-      *reinterpret_cast<h8*>(As + r * LDA + w * 8) = p;
-    }
+  for (int i = 0; i < PD; ++i) load(reg[i], i);
+  store(reg[0], 0, 0);
+  __syncthreads();
+  for (int j = 0; j < ns; j += U) {
 #pragma unroll
-    for (int i = 0; i < C::B_VEC; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int r = idx / (BK / 32), w = idx % (BK / 32);
-      const uint32_t wv[4] = {breg[i].x, breg[i].y, breg[i].z, breg[i].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t u = wv[t];
-        uint4 o;
-        o.x = dq2(u, zreg[i]);        // ch 0, 4
-        o.y = dq2(u >> 4, zreg[i]);   // ch 1, 5
-        o.z = dq2(u >> 8, zreg[i]);   // ch 2, 6
-        o.w = dq2(u >> 12, zreg[i]);  // ch 3, 7
-        *reinterpret_cast<uint4*>(Bs + r * LDA + w * 32 + t * 8) = o;
+    for (int u = 0; u < U; ++u) {
+      const int t = j + u;
+      if (u < 2 || t < ns) {  // ns is even: the first two steps always run
+        load(reg[u % PD], t + PD);
+        __builtin_amdgcn_sched_barrier(0);  // issue the loads before the stage's MFMAs
+        compute(u & 1, (u & 1) == 0);
+        if (u + 1 < U || t + 1 < ns) {
+          if (t + 1 < ns) store(reg[(u + 1) % PD], (u + 1) & 1, t + 1);
+        }
+        __syncthreads();
       }
-      if (w == 0) Ss[r] = sreg[i];
-    }
-  };
-
-  f4 acc[C::TM][C::TN];
-  f4 accg[C::TM][C::TN];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
-  load_group(0);
-  for (int g = 0; g < G; ++g) {
-    __syncthreads();
-    store_group();
-    __syncthreads();
-    if (g + 1 < G) load_group(g + 1);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) accg[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      h8 af[C::TM], bf[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        af[i] = *reinterpret_cast<const h8*>(As + (wm * C::TM * 16 + i * 16 + lrow) * LDA + kk + lk);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        bf[j] = *reinterpret_cast<const h8*>(Bs + (wn * C::TN * 16 + j * 16 + lrow) * LDA + kk + lk);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          accg[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], accg[i][j], 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const float sc = Ss[wn * C::TN * 16 + j * 16 + lrow];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) acc[i][j] += sc * accg[i][j];
     }
   }
 
-  // C tile layout of v_mfma_f32_16x16x32_f16: lane holds column (lane & 15),
-  // rows 4 * (lane >> 4) + r, r = 0..3.
+  // ---- epilogue: multiply by the last group's scale and store (or store the split's partial)
+  float* Sf = reinterpret_cast<float*>(smem);  // [BN]; both buffers are idle after the barrier
+  if (tid < BN) Sf[tid] = prev_s;
+  __syncthreads();
+  const bool part = p.splits > 1;
+  const size_t obase = part ? size_t(split) * size_t(M) * size_t(N) : 0;
+  const size_t ld = part ? size_t(N) : size_t(p.ldy);
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+  for (int j = 0; j < T::TN; ++j) {
+    const int nl = wn * (BN / T::WN) + j * 32 + l32;
+    const int n = n0 + nl;
+    const float sl = Sf[nl];
+    if (n >= N) continue;
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int n = n0 + wn * C::TN * 16 + j * 16 + lrow;
+    for (int i = 0; i < T::TM; ++i) {
+      const int mb = m0 + wm * (BM / WM) + i * 32 + 4 * hh;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * C::TM * 16 + i * 16 + (lane >> 4) * 4 + r;
-        if (m < M && n < N) {
-          if (ydtype == PARO_F32)
-            static_cast<float*>(y)[size_t(m) * N + n] = acc[i][j][r];
+      for (int v = 0; v < 16; ++v) {
+        const int m = mb + 8 * (v >> 2) + (v & 3);
+        if (m < M) {
+          const float val = acc[i][j][v] * sl;
+          const size_t o = obase + size_t(m) * ld + size_t(n);
+          if (part)
+            p.part[o] = val;
+          else if (p.ydtype == PARO_F32)
+            static_cast<float*>(p.y)[o] = val;
           else
-            static_cast<_Float16*>(y)[size_t(m) * N + n] = static_cast<_Float16>(acc[i][j][r]);
+            static_cast<_Float16*>(p.y)[o] = static_cast<_Float16>(val);
         }
       }
     }
+  }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(int M, int D, int N, const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
-                      const uint16_t* zeros, void* y, int ydtype, hipStream_t st) {
-  using C = Cfg<BM, BN, WM, WN>;
-  if (C::kLds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(C::kLds));
+// y = sum over the S split partials [S][M][N], in split order; y rows are ldy elements apart.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, void* __restrict__ y,
+                                                            int M, int N, int ldy, int S, int ydtype) {
+  const size_t count = size_t(M) * size_t(N);
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t e = size_t(blockIdx.x) * blockDim.x + threadIdx.x; e < count; e += stride) {
+    float v = part[e];
+    for (int s = 1; s < S; ++s) v += part[size_t(s) * count + e];
+    const size_t m = e / size_t(N), n = e - m * size_t(N);
+    const size_t o = m * size_t(ldy) + n;
+    if (ydtype == PARO_F32)
+      static_cast<float*>(y)[o] = v;
+    else
+      static_cast<_Float16*>(y)[o] = static_cast<_Float16>(v);
+  }
+}
+
+template <int BM, int BN, int WM, int PD, bool APERM>
+hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
+  using T = Tile<BM, BN, WM>;
+  const void* fn = reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, PD, APERM>);
+  if (T::LDS > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(T::LDS));
     if (e != hipSuccess) return e;
   }
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN>), grid, dim3(C::kThreads), C::kLds, st, M, D, N, x, qweight,
-                     scales, zeros, y, ydtype);
+  const int grid = a.tiles_m * a.tiles_n * a.splits;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, PD, APERM>), dim3(grid), dim3(kThreads), T::LDS, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int M, int D, int N, const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
-                       const uint16_t* zeros, void* y, int ydtype, hipStream_t st) {
-  if (M <= 16) return launch_cfg<16, 64, 1, 4>(M, D, N, x, qweight, scales, zeros, y, ydtype, st);
-  if (M <= 64) return launch_cfg<64, 64, 2, 2>(M, D, N, x, qweight, scales, zeros, y, ydtype, st);
-  return launch_cfg<128, 128, 2, 2>(M, D, N, x, qweight, scales, zeros, y, ydtype, st);
+GemmPlan plan_gemm(int M, int D, int N) {
+  // Candidate tilings with their measured throughput per CU on MI355X (TFLOP/s with two or
+  // more resident workgroups per CU, i.e. two waves per SIMD, which hides the VALU work of the
+  // in-register dequant under the MFMAs; one resident workgroup reaches about 0.7 of it).
+  struct Cand {
+    int BM, BN, WM, occ;  // occ: workgroups a CU holds at once (registers and LDS)
+    double rate;
+  };
+  static const Cand cands[] = {{128, 256, 1, 2, 3.5}, {128, 192, 2, 2, 3.2}, {128, 128, 2, 3, 3.15},
+                               {128, 128, 1, 3, 3.1}, {64, 256, 1, 3, 2.9},   {64, 128, 2, 4, 2.6}};
+  const int G = D / PARO_GROUP;
+  GemmPlan best{128, 128, 2, 2, 1};
+  double best_t = 1e300;
+  for (const Cand& c : cands) {
+    const long tiles = long((M + c.BM - 1) / c.BM) * ((N + c.BN - 1) / c.BN);
+    for (int S = 1; S <= 8; ++S) {
+      const int gps = (G + S - 1) / S;
+      if (S > 1 && (S - 1) * gps >= G) continue;  // every split must own a group
+      const long wgs = tiles * S;
+      const long per_cu = (wgs + 255) / 256;            // workgroups the busiest CU runs
+      const double rate = per_cu >= 2 ? c.rate : 0.7 * c.rate;
+      const double wg_flop = 2.0 * c.BM * c.BN * 128.0 * gps;
+      const double t_mfma = double(per_cu) * wg_flop / (rate * 1e12);
+      // split partials: written and read back once (about 6 TB/s) plus the reduction launch
+      const double t_split = S > 1 ? double(S) * M * N * 8.0 / 6e12 + 3e-6 : 0.0;
+      const double t = t_mfma + t_split;
+      if (t < best_t * 0.98) {
+        best_t = t;
+        best = GemmPlan{c.BM, c.BN, c.WM, 2, S};
+      }
+    }
+  }
+  return best;
+}
+
+size_t gemm_workspace_bytes(int M, int D, int N) {
+  const GemmPlan g = plan_gemm(M, D, N);
+  return g.splits > 1 ? align256(size_t(g.splits) * M * N * 4) : 0;
+}
+
+namespace {
+
+// One launch over rows [0, M) and columns [0, N) of the operands as given (y rows ldy apart);
+// the caller keeps every byte offset of the kernel below 4 GiB.
+hipError_t launch_block(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, void* y, int ldy, int ydtype, void* ws,
+                        size_t ws_bytes, hipStream_t st) {
+  GemmPlan g = plan_gemm(M, D, N);
+  if (g.splits > 1 && ws_bytes < size_t(g.splits) * M * N * 4) g.splits = 1;  // no room for partials
+  GemmArgs a;
+  a.x = x;
+  a.qw = qweight;
+  a.sc = scales;
+  a.zr = zeros;
+  a.y = y;
+  a.part = static_cast<float*>(ws);
+  a.M = M;
+  a.D = D;
+  a.N = N;
+  a.G = D / PARO_GROUP;
+  a.tiles_m = (M + g.BM - 1) / g.BM;
+  a.tiles_n = (N + g.BN - 1) / g.BN;
+  a.splits = g.splits;
+  a.gps = (a.G + g.splits - 1) / g.splits;
+  a.ydtype = ydtype;
+  a.ldy = ldy;
+  hipError_t e = hipErrorInvalidValue;
+#define PARO_GEMM_CASE(bm, bn, wm, pd)                                                                      \
+  if (g.BM == bm && g.BN == bn && g.WM == wm && g.PD == pd)                                                 \
+    e = x_nibble_order ? launch_tile<bm, bn, wm, pd, true>(a, st) : launch_tile<bm, bn, wm, pd, false>(a, st);
+  PARO_GEMM_CASE(128, 256, 1, 2)
+  PARO_GEMM_CASE(128, 128, 1, 2)
+  PARO_GEMM_CASE(128, 128, 1, 3)
+  PARO_GEMM_CASE(64, 256, 1, 2)
+  PARO_GEMM_CASE(64, 256, 1, 3)
+  PARO_GEMM_CASE(128, 192, 2, 2)
+  PARO_GEMM_CASE(128, 128, 2, 2)
+  PARO_GEMM_CASE(128, 128, 2, 3)
+  PARO_GEMM_CASE(64, 256, 2, 2)
+  PARO_GEMM_CASE(64, 192, 2, 2)
+  PARO_GEMM_CASE(64, 128, 2, 2)
+#undef PARO_GEMM_CASE
+  if (e != hipSuccess || g.splits == 1) return e;
+  const size_t count = size_t(M) * N;
+  const int blocks = int(std::min<size_t>((count + 255) / 256, 4096));
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, static_cast<const float*>(ws), y, M, N,
+                     ldy, g.splits, ydtype);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
+                       const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, void* ws,
+                       size_t ws_bytes, hipStream_t st) {
+  // The kernel addresses x, the packed weights, scales and zeros with 32-bit byte offsets:
+  // split the call into blocks of rows and columns that keep each operand below 4 GiB.
+  const size_t lim = (size_t(1) << 32) - 1, ysz = ydtype == PARO_F32 ? 4 : 2;
+  const long rows = std::min<long>(M, long(lim / (size_t(D) * 2)) / 256 * 256);
+  const long cols = std::min<long>(N, long(lim / (size_t(D) / 2)) / 256 * 256);
+  const size_t G = size_t(D / PARO_GROUP);
+  for (long r0 = 0; r0 < M; r0 += rows)
+    for (long c0 = 0; c0 < N; c0 += cols) {
+      const int mr = int(std::min<long>(rows, M - r0)), nc = int(std::min<long>(cols, N - c0));
+      hipError_t e = launch_block(mr, D, nc, x + size_t(r0) * D, x_nibble_order, qweight + size_t(c0) * D / 2,
+                                  scales + size_t(c0) * G, zeros + size_t(c0) * G,
+                                  static_cast<char*>(y) + (size_t(r0) * N + size_t(c0)) * ysz, N, ydtype, ws,
+                                  ws_bytes, st);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
 }
 
 }  // namespace paro

@@ -33,11 +33,17 @@ paro_status check_rotation(const paro_rotation* r) {
 
 paro_status from_hip(hipError_t e) { return e == hipSuccess ? PARO_OK : PARO_EHIP; }
 
-// Workspace of one rotated call: the transformed x, unless the transform runs inside the
-// decode kernel.
+// Workspace of one plain linear: the GEMM's split partial sums (decode-shaped calls take none).
+size_t linear_ws_bytes(int M, int D, int N) {
+  if (M <= 0 || N <= 0 || decode_takes(-1, M, D, N)) return 0;
+  return gemm_workspace_bytes(M, D, N);
+}
+
+// Workspace of one rotated call: the transformed x, then the linear's own workspace, unless the
+// transform runs inside the decode kernel.
 size_t rotated_ws_bytes(int K, int M, int D, int N) {
   if (M <= 0 || N <= 0 || decode_takes(K, M, D, N)) return 0;
-  return align256(size_t(M) * size_t(D) * 2);
+  return align256(size_t(M) * size_t(D) * 2) + linear_ws_bytes(M, D, N);
 }
 
 paro_status check_linear_args(int M, int D, int N, const void* x, const uint8_t* qweight,
@@ -187,38 +193,51 @@ paro_status paro_rotate(const paro_rotation* r, int M, const void* x, void* xout
 
 size_t paro_workspace_bytes(int M, int D, int N) {
   if (M <= 0 || N < 0 || check_shape(0, D) != PARO_OK) return 0;
-  return align256(size_t(M) * size_t(D) * 2);  // enough for every transform (K) and path
+  // enough for every transform (K) and path: the transformed x, then the GEMM's partial sums
+  return align256(size_t(M) * size_t(D) * 2) + linear_ws_bytes(M, D, N);
 }
 
 static paro_status run_linear(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
-                              const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, hipStream_t st) {
+                              const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, void* ws,
+                              size_t ws_bytes, hipStream_t st) {
   if (decode_takes(-1, M, D, N)) {
     const DecodeCall c{nullptr, M, N, x, x_nibble_order, qweight, scales, zeros, y};
     return from_hip(launch_decode(D, ydtype, &c, 1, st));
   }
-  return from_hip(launch_gemm(M, D, N, x, qweight, scales, zeros, y, ydtype, st));
+  return from_hip(launch_gemm(M, D, N, x, x_nibble_order, qweight, scales, zeros, y, ydtype, ws, ws_bytes, st));
 }
 
 // A rotated call that the decode kernel cannot take: transform into the workspace, then the
-// linear on it (the decode kernel takes the workspace in its word order).
+// linear on it (both linear kernels take the transformed x in their word order). The rest of
+// the workspace, after the transformed x, is the linear's.
 static paro_status run_rotated_two_step(const DevRot& R, int M, int N, const uint16_t* x, const uint8_t* qweight,
                                         const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype,
-                                        uint16_t* xr, hipStream_t st) {
+                                        void* ws, size_t ws_bytes, hipStream_t st) {
   const int D = R.D;
-  const bool nib = decode_takes(-1, M, D, N);
-  if (hipError_t e = launch_rotate(R, M, x, xr, nib, st)) return from_hip(e);
-  return run_linear(M, D, N, xr, nib, qweight, scales, zeros, y, ydtype, st);
+  uint16_t* xr = static_cast<uint16_t*>(ws);
+  const size_t xr_bytes = align256(size_t(M) * size_t(D) * 2);
+  if (hipError_t e = launch_rotate(R, M, x, xr, true, st)) return from_hip(e);
+  return run_linear(M, D, N, xr, true, qweight, scales, zeros, y, ydtype, static_cast<char*>(ws) + xr_bytes,
+                    ws_bytes - xr_bytes, st);
 }
 
 paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t* qweight, const void* scales,
                               const void* zeros, void* y, int ydtype, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (paro_status s = check_shape(0, D)) return s;
   if (paro_status s = check_linear_args(M, D, N, x, qweight, scales, zeros, y, ydtype)) return s;
   if (M == 0 || N == 0) return PARO_OK;
+  const size_t need = linear_ws_bytes(M, D, N);
+  if (!ws) ws_bytes = 0;
+  if (need && ws_bytes >= need) {  // room for the split partial sums: they must not overlap any operand
+    if (!aligned16(ws)) return PARO_EINVAL;
+    const size_t G = size_t(D / PARO_GROUP);
+    if (overlap(ws, need, x, size_t(M) * D * 2) || overlap(ws, need, y, size_t(M) * size_t(N) * (ydtype ? 4 : 2)) ||
+        overlap(ws, need, qweight, size_t(N) * D / 2) || overlap(ws, need, scales, size_t(N) * G * 2) ||
+        overlap(ws, need, zeros, size_t(N) * G * 2))
+      return PARO_EINVAL;
+  }
   return run_linear(M, D, N, static_cast<const uint16_t*>(x), false, qweight, static_cast<const uint16_t*>(scales),
-                    static_cast<const uint16_t*>(zeros), y, ydtype, static_cast<hipStream_t>(stream));
+                    static_cast<const uint16_t*>(zeros), y, ydtype, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void* x, const uint8_t* qweight,
@@ -242,7 +261,7 @@ paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void
   if (!aligned16(ws)) return PARO_EINVAL;
   const size_t ybytes = size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2);
   if (overlap(ws, need, x, size_t(M) * D * 2) || overlap(ws, need, y, ybytes)) return PARO_EINVAL;
-  return run_rotated_two_step(R, M, N, xh, qweight, sc, zr, y, ydtype, static_cast<uint16_t*>(ws), st);
+  return run_rotated_two_step(R, M, N, xh, qweight, sc, zr, y, ydtype, ws, need, st);
 }
 
 // ---- batches -------------------------------------------------------------------------------
@@ -250,7 +269,8 @@ paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void
 static size_t batch_ws_bytes(int count, const paro_linear_args* calls) {
   size_t total = 0;
   for (int i = 0; i < count; ++i)
-    if (calls[i].rot) total += rotated_ws_bytes(calls[i].rot->K, calls[i].M, calls[i].D, calls[i].N);
+    total += calls[i].rot ? rotated_ws_bytes(calls[i].rot->K, calls[i].M, calls[i].D, calls[i].N)
+                          : linear_ws_bytes(calls[i].M, calls[i].D, calls[i].N);
   return total;
 }
 
@@ -336,10 +356,13 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     paro_status s;
     if (c.rot) {
       const DevRot R = dev_rot(*c.rot);
-      s = run_rotated_two_step(R, c.M, c.N, xh, c.qweight, sc, zr, c.y, ydtype, reinterpret_cast<uint16_t*>(wsp), st);
-      wsp += rotated_ws_bytes(R.K, c.M, c.D, c.N);
+      const size_t part = rotated_ws_bytes(R.K, c.M, c.D, c.N);
+      s = run_rotated_two_step(R, c.M, c.N, xh, c.qweight, sc, zr, c.y, ydtype, wsp, part, st);
+      wsp += part;
     } else {
-      s = run_linear(c.M, c.D, c.N, xh, false, c.qweight, sc, zr, c.y, ydtype, st);
+      const size_t part = linear_ws_bytes(c.M, c.D, c.N);
+      s = run_linear(c.M, c.D, c.N, xh, false, c.qweight, sc, zr, c.y, ydtype, wsp, part, st);
+      wsp += part;
     }
     if (s != PARO_OK) return s;
   }

@@ -119,7 +119,20 @@ hipError_t launch_pack(const DevRot& R, int N, const uint16_t* W, uint8_t* qweig
 // nibble_order: write each 8-channel word as [0,4,1,5,2,6,3,7] (the decode kernel's A order).
 hipError_t launch_rotate(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, bool nibble_order,
                          hipStream_t st);
-hipError_t launch_gemm(int M, int D, int N, const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
-                       const uint16_t* zeros, void* y, int ydtype, hipStream_t st);
+// Tiling of the prefill GEMM (gemm.hip): a BM x BN output tile per workgroup, the reduction
+// over D split into `splits` ranges of groups whose float32 partial sums a second kernel adds.
+struct GemmPlan {
+  int BM, BN, WM, PD, splits;  // WM: rows of the 2 x 2 (WM = 2) or 1 x 4 (WM = 1) wave grid;
+                               // PD: stages of global loads in flight
+};
+GemmPlan plan_gemm(int M, int D, int N);
+// Workspace bytes the GEMM's split partial sums take at (M, D, N) (0: no split).
+size_t gemm_workspace_bytes(int M, int D, int N);
+// x_nibble_order: x's 8-channel words are already in the decode order [0,4,1,5,2,6,3,7].
+// ws / ws_bytes: room for the split partial sums; with less than gemm_workspace_bytes the
+// reduction is not split.
+hipError_t launch_gemm(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
+                       const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, void* ws,
+                       size_t ws_bytes, hipStream_t st);
 
 }  // namespace paro

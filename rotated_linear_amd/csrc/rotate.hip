@@ -2,84 +2,103 @@
 // then division by the channel scales ("ParoQuant: pairwise rotations that
 // survive deployment", section "A rotation small enough to execute").
 //
-// One workgroup of 512 threads transforms R rows held in LDS as float32 for all
-// K stages (rotation_core.h). Stage parameters stream through a register ring
-// issued before the rows are even loaded; 1/s is applied on the way out with one
-// float32 -> float16 rounding. With PERM the output keeps every 8-channel word in
-// the order the INT4 decode of the linear kernels produces ([0,4,1,5,2,6,3,7]),
-// which is how paro_rotated_linear hands its workspace to them.
+// One workgroup of 512 threads holds R rows in LDS as float32, interleaved by
+// channel (lds[c * R + r]: one R-wide vector per channel, so a stage moves a pair
+// of channels for all R rows with two vector reads and two vector writes), runs
+// the K stages (rotation_core.h) and writes fp16(rows * (1/s)). Workgroups are
+// persistent over blocks of R rows. Stage parameters stream through a register
+// ring issued before the block's rows are loaded.
+//
+// LDS banks (32 on gfx950): inside a stage, the host's pair order keeps the channels
+// of 8 (16, 32) consecutive lanes distinct modulo 8 (16, 32), so the R = 4 (2, 1)
+// vector accesses are conflict-free; rows move between global memory and LDS with
+// one channel per lane, so a wave's vector accesses cover consecutive channels.
+//
+// With PERM the output keeps every 8-channel word in the order the INT4 decode of
+// the linear kernels produces ([0,4,1,5,2,6,3,7]), which is how
+// paro_rotated_linear hands its workspace to them.
+#include <algorithm>
+
 #include "rotation_core.h"
 
 namespace paro {
 namespace {
 
 constexpr int kRotThreads = 512;
+constexpr size_t kRotLds = 160 * 1024;
+constexpr int kCUs = 256;
 
 template <int R, int PPT, int PD, bool EXACT, bool PERM>
 __global__ __launch_bounds__(kRotThreads) void rotate_rows_kernel(const uint16_t* __restrict__ x,
                                                                    uint16_t* __restrict__ xout, int M, int D,
-                                                                   int K, const PairRec* __restrict__ recs,
+                                                                   int K, const PairRec* recs,
                                                                    const float* __restrict__ inv_s) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [D][R]
   const int tid = threadIdx.x;
-  const int row0 = blockIdx.x * R;
   const int P = D / 2;
-  const int words = D / 8;  // 16-byte words per row
-  const int total = words * R;
+  const int nblk = (M + R - 1) / R;
 
-  StageRing<kRotThreads, PPT, PD, EXACT> ring;
-  if (K > 0) ring_prime(ring, K, P, tid, recs);
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int row0 = blk * R;
+    StageRing<kRotThreads, PPT, PD, EXACT> ring;
+    if (K > 0) ring_prime(ring, K, P, tid, recs);
 
-  // rows -> LDS, four 16-byte loads in flight per thread per batch
-  for (int base = 0; base < total; base += 4 * kRotThreads) {
-    uint4 v[4];
+    // rows -> LDS: lane = channel, so a wave writes 64 consecutive channel vectors (distinct
+    // bank groups) and reads 64 consecutive halves of each row
+    using V = typename RowVec<R>::T;
+    V* rows = reinterpret_cast<V*>(lds);
+    const uint16_t* xr[R];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int e = base + tid + u * kRotThreads;
-      e = e < total ? e : total - 1;
-      const int r = e / words, w = e - r * words;
-      int row = row0 + r;
-      row = row < M ? row : M - 1;
-      v[u] = *reinterpret_cast<const uint4*>(x + size_t(row) * D + size_t(w) * 8);
-    }
+    for (int r = 0; r < R; ++r) xr[r] = x + size_t(min(row0 + r, M - 1)) * D;
+    constexpr int UB = 8;  // channels per thread whose loads are in flight together
+    for (int c0 = tid; c0 < D; c0 += UB * kRotThreads) {
+      uint16_t hv[UB][R];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = base + tid + u * kRotThreads;
-      if (e < total) {
-        const int r = e / words, w = e - r * words;
-        const _Float16* h = reinterpret_cast<const _Float16*>(&v[u]);
+      for (int u = 0; u < UB; ++u) {
+        const int c = min(c0 + u * kRotThreads, D - 1);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) lds[(w * 8 + t) * R + r] = static_cast<float>(h[t]);
+        for (int r = 0; r < R; ++r) hv[u][r] = xr[r][c];
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int c = c0 + u * kRotThreads;
+        if (c < D) {
+          float f[R];
+#pragma unroll
+          for (int r = 0; r < R; ++r) f[r] = static_cast<float>(__builtin_bit_cast(_Float16, hv[u][r]));
+          rows[c] = *reinterpret_cast<const V*>(f);
+        }
       }
     }
-  }
-  __syncthreads();
-  if (K > 0) ring_run<R>(ring, lds, K, P, tid, recs);
+    __syncthreads();
+    if (K > 0) ring_run<R>(ring, lds, K, P, tid, recs);  // ends with a barrier
 
-  for (int e = tid; e < total; e += kRotThreads) {
-    const int r = e / words, w = e - r * words;
-    const int row = row0 + r;
-    if (row >= M) continue;
-    _Float16 h[8];
+    // LDS -> fp16(rows * (1/s)), rows below M only; lane = channel as above
+    for (int c = tid; c < D; c += kRotThreads) {
+      const V v = rows[c];
+      const float is = inv_s[c];
+      const int pos = PERM ? (c & ~7) | nib_slot(c & 7) : c;
+      const float* f = reinterpret_cast<const float*>(&v);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = w * 8 + u;
-      h[PERM ? nib_slot(u) : u] = static_cast<_Float16>(lds[c * R + r] * inv_s[c]);
+      for (int r = 0; r < R; ++r)
+        if (row0 + r < M) xout[size_t(row0 + r) * D + pos] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f[r] * is));
     }
-    *reinterpret_cast<uint4*>(xout + size_t(row) * D + size_t(w) * 8) = *reinterpret_cast<const uint4*>(h);
+    __syncthreads();  // the next block overwrites the rows
   }
 }
 
 template <int R, int PPT, int PD, bool EXACT, bool PERM>
 hipError_t launch_rows(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
   const size_t lds = size_t(Rt.D) * R * sizeof(float);
+  const void* fn = reinterpret_cast<const void*>(&rotate_rows_kernel<R, PPT, PD, EXACT, PERM>);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rotate_rows_kernel<R, PPT, PD, EXACT, PERM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  const int blocks = (M + R - 1) / R;
-  hipLaunchKernelGGL((rotate_rows_kernel<R, PPT, PD, EXACT, PERM>), dim3(blocks), dim3(kRotThreads), lds, st, x,
+  const long nblk = (M + R - 1) / R;
+  const long per_cu = std::max<long>(1, long(kRotLds / lds));  // workgroups one CU holds at once
+  const int grid = int(std::min<long>(nblk, per_cu * kCUs));
+  hipLaunchKernelGGL((rotate_rows_kernel<R, PPT, PD, EXACT, PERM>), dim3(grid), dim3(kRotThreads), lds, st, x,
                      xout, M, Rt.D, Rt.K, Rt.rec, Rt.inv_s);
   return hipGetLastError();
 }
@@ -90,26 +109,36 @@ hipError_t launch_exact(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xo
   return launch_rows<R, PPT, PD, false, PERM>(Rt, M, x, xout, st);
 }
 
+// Pairs per thread per stage (PPT) and its ring depth; R rows take PPT up to kMaxPpt<R>
+// (beyond it the float32 rows and the records outgrow the registers).
+template <int R>
+constexpr int kMaxPpt = R == 4 ? 9 : 16;
+
 template <int R, bool PERM>
 hipError_t launch_ppt(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  const int ppt = (Rt.D / 2 + kRotThreads - 1) / kRotThreads;  // pairs per thread per stage
+  const int ppt = (Rt.D / 2 + kRotThreads - 1) / kRotThreads;
   if (ppt <= 1) return launch_exact<R, 1, 8, PERM>(Rt, M, x, xout, st);
   if (ppt <= 2) return launch_exact<R, 2, 8, PERM>(Rt, M, x, xout, st);
-  if (ppt <= 3) return launch_exact<R, 3, 8, PERM>(Rt, M, x, xout, st);
+  if (ppt <= 3) return launch_exact<R, 3, 4, PERM>(Rt, M, x, xout, st);
   if (ppt <= 4) return launch_exact<R, 4, 4, PERM>(Rt, M, x, xout, st);
-  if (ppt <= 6) return launch_exact<R, 6, 4, PERM>(Rt, M, x, xout, st);
+  if (ppt <= 6) return launch_exact<R, 6, 2, PERM>(Rt, M, x, xout, st);
   if (ppt <= 9) return launch_exact<R, 9, 2, PERM>(Rt, M, x, xout, st);
-  if (ppt <= 12) return launch_exact<R, 12, 2, PERM>(Rt, M, x, xout, st);
-  return launch_exact<R, 16, 2, PERM>(Rt, M, x, xout, st);
+  if constexpr (kMaxPpt<R> >= 12)
+    if (ppt <= 12) return launch_exact<R, 12, 2, PERM>(Rt, M, x, xout, st);
+  if constexpr (kMaxPpt<R> >= 14)
+    if (ppt <= 14) return launch_exact<R, 14, 1, PERM>(Rt, M, x, xout, st);
+  if constexpr (kMaxPpt<R> >= 16) return launch_exact<R, 16, 1, PERM>(Rt, M, x, xout, st);
+  return hipErrorInvalidValue;
 }
 
 template <bool PERM>
 hipError_t launch_r(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  // Rows per workgroup: amortize the stage parameters over several rows once there are
-  // enough rows to keep >= 512 workgroups, within 80 KB of LDS (two workgroups per CU).
+  // Rows per workgroup: a stage's parameters are read once per block, so larger blocks
+  // save their traffic once there are enough rows to give every CU a block.
   const size_t row_bytes = size_t(R.D) * 4;
-  if (M >= 4 * 512 && 4 * row_bytes <= 80 * 1024) return launch_ppt<4, PERM>(R, M, x, xout, st);
-  if (M >= 2 * 512 && 2 * row_bytes <= 80 * 1024) return launch_ppt<2, PERM>(R, M, x, xout, st);
+  const int ppt = (R.D / 2 + kRotThreads - 1) / kRotThreads;
+  if (M >= 4 * kCUs && 4 * row_bytes <= kRotLds && ppt <= kMaxPpt<4>) return launch_ppt<4, PERM>(R, M, x, xout, st);
+  if (M >= 2 * kCUs && 2 * row_bytes <= kRotLds && ppt <= kMaxPpt<2>) return launch_ppt<2, PERM>(R, M, x, xout, st);
   return launch_ppt<1, PERM>(R, M, x, xout, st);
 }
 

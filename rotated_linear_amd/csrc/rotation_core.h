@@ -38,20 +38,29 @@ template <int NT, int PPT, int PD, bool EXACT, bool TIGHT = false>
 struct StageRing {
   PairRec rec[PD][PPT];
 
-  // Issue the loads of stage k (clamped into [0, K)) into ring slot `slot`.
+  // Issue the loads of stage k (clamped into [0, K)) into ring slot `slot`: a uniform stage
+  // base plus a 32-bit per-lane byte offset (the same offsets serve every stage, so no
+  // per-stage addresses stay live in registers).
   template <int slot, class RP>
   __device__ inline void issue(int k, int K, int P, int tid, RP recs) {
     int kc = k < K ? k : K - 1;
     kc = kc > 0 ? kc : 0;  // K == 0: reads stay inside the descriptor and are never used
-    const size_t base = size_t(kc) * size_t(P);
+    typedef __attribute__((address_space(1))) const unsigned char* gbytes;
+    uintptr_t stage_base = reinterpret_cast<uintptr_t>(&recs[0]) + size_t(kc) * size_t(P) * sizeof(PairRec);
+    // opaque here: the per-lane addresses of a stage are formed where its loads issue, instead of
+    // every stage's being computed up front (and kept live) by loop-invariant hoisting
+    asm volatile("" : "+s"(stage_base));
+    const gbytes sb = reinterpret_cast<gbytes>(stage_base);
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
       int p = tid + q * NT;
       if constexpr (!EXACT) p = p < P ? p : P - 1;
-      const auto& r = recs[base + p];  // field by field: recs may be a global-address-space pointer
-      rec[slot][q].ij = r.ij;
-      rec[slot][q].c = r.c;
-      rec[slot][q].s = r.s;
+      // three 4-byte-aligned words (a 12-byte record; one dwordx3 load)
+      typedef __attribute__((address_space(1))) const uint32_t* gwords;
+      const gwords w = reinterpret_cast<gwords>(sb + uint32_t(p) * uint32_t(sizeof(PairRec)));
+      rec[slot][q].ij = w[0];
+      rec[slot][q].c = __builtin_bit_cast(float, w[1]);
+      rec[slot][q].s = __builtin_bit_cast(float, w[2]);
     }
   }
 
