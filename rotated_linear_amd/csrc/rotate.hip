@@ -11,8 +11,9 @@
 //
 // LDS banks (32 on gfx950): inside a stage, the host's pair order keeps the channels
 // of 8 (16, 32) consecutive lanes distinct modulo 8 (16, 32), so the R = 4 (2, 1)
-// vector accesses are conflict-free; rows move between global memory and LDS with
-// one channel per lane, so a wave's vector accesses cover consecutive channels.
+// vector accesses are conflict-free. Rows move between global memory and LDS two
+// adjacent channels per lane (4-byte accesses, every load of a block in flight at
+// once), so a wave's vector accesses cover consecutive channels.
 //
 // With PERM the output keeps every 8-channel word in the order the INT4 decode of
 // the linear kernels produces ([0,4,1,5,2,6,3,7]), which is how
@@ -43,45 +44,76 @@ __global__ __launch_bounds__(kRotThreads) void rotate_rows_kernel(const uint16_t
     StageRing<kRotThreads, PPT, PD, EXACT> ring;
     if (K > 0) ring_prime(ring, K, P, tid, recs);
 
-    // rows -> LDS: lane = channel, so a wave writes 64 consecutive channel vectors (distinct
-    // bank groups) and reads 64 consecutive halves of each row
+    // rows -> LDS: lane = two adjacent channels (one 4-byte load per row, all of the thread's
+    // loads in flight at once); a wave writes 128 consecutive channel vectors
     using V = typename RowVec<R>::T;
     V* rows = reinterpret_cast<V*>(lds);
-    const uint16_t* xr[R];
+    uintptr_t xb = reinterpret_cast<uintptr_t>(x);
+    asm volatile("" : "+s"(xb));  // as for 1/s below: addresses formed where the loads issue
+    const uint32_t* xr[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) xr[r] = x + size_t(min(row0 + r, M - 1)) * D;
-    constexpr int UB = 8;  // channels per thread whose loads are in flight together
-    for (int c0 = tid; c0 < D; c0 += UB * kRotThreads) {
-      uint16_t hv[UB][R];
+    for (int r = 0; r < R; ++r)
+      xr[r] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(xb) + size_t(min(row0 + r, M - 1)) * D);
+    {
+      uint32_t hv[PPT][R];  // channel pair cp = tid + u * NT: channels 2 cp (low half), 2 cp + 1
 #pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        const int c = min(c0 + u * kRotThreads, D - 1);
+      for (int u = 0; u < PPT; ++u) {
+        const int cp = min(tid + u * kRotThreads, P - 1);
 #pragma unroll
-        for (int r = 0; r < R; ++r) hv[u][r] = xr[r][c];
+        for (int r = 0; r < R; ++r) hv[u][r] = xr[r][cp];
       }
 #pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        const int c = c0 + u * kRotThreads;
-        if (c < D) {
-          float f[R];
+      for (int u = 0; u < PPT; ++u) {
+        const int cp = tid + u * kRotThreads;
+        if (cp < P) {
+          float f0[R], f1[R];
 #pragma unroll
-          for (int r = 0; r < R; ++r) f[r] = static_cast<float>(__builtin_bit_cast(_Float16, hv[u][r]));
-          rows[c] = *reinterpret_cast<const V*>(f);
+          for (int r = 0; r < R; ++r) {
+            f0[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r])));
+            f1[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r] >> 16)));
+          }
+          rows[2 * cp] = *reinterpret_cast<const V*>(f0);
+          rows[2 * cp + 1] = *reinterpret_cast<const V*>(f1);
         }
       }
     }
     __syncthreads();
     if (K > 0) ring_run<R>(ring, lds, K, P, tid, recs);  // ends with a barrier
 
-    // LDS -> fp16(rows * (1/s)), rows below M only; lane = channel as above
-    for (int c = tid; c < D; c += kRotThreads) {
-      const V v = rows[c];
-      const float is = inv_s[c];
-      const int pos = PERM ? (c & ~7) | nib_slot(c & 7) : c;
-      const float* f = reinterpret_cast<const float*>(&v);
+    // LDS -> fp16(rows * (1/s)), rows below M only; lane = channel pair as above. The thread's
+    // 1/s values are loaded together first (one memory round trip per block).
+    {
+      // the base is made opaque per block so the loads' addresses are formed here, not hoisted
+      // out of the block loop and kept live (or spilled) across the stages
+      uintptr_t isb = reinterpret_cast<uintptr_t>(inv_s), ob = reinterpret_cast<uintptr_t>(xout);
+      asm volatile("" : "+s"(isb), "+s"(ob));
+      float2 isv[PPT];
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (row0 + r < M) xout[size_t(row0 + r) * D + pos] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f[r] * is));
+      for (int u = 0; u < PPT; ++u) isv[u] = reinterpret_cast<const float2*>(isb)[min(tid + u * kRotThreads, P - 1)];
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        const int cp = tid + u * kRotThreads;
+        if (cp < P) {
+          const V v0 = rows[2 * cp], v1 = rows[2 * cp + 1];
+          const float* f0 = reinterpret_cast<const float*>(&v0);
+          const float* f1 = reinterpret_cast<const float*>(&v1);
+          const int c = 2 * cp;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if (row0 + r < M) {
+              const uint16_t h0 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f0[r] * isv[u].x));
+              const uint16_t h1 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f1[r] * isv[u].y));
+              uint16_t* out = reinterpret_cast<uint16_t*>(ob) + size_t(row0 + r) * D;
+              if constexpr (PERM) {  // channels c, c + 1 sit apart in the decode order
+                out[(c & ~7) | nib_slot(c & 7)] = h0;
+                out[(c & ~7) | nib_slot((c + 1) & 7)] = h1;
+              } else {
+                reinterpret_cast<uint32_t*>(out)[cp] = uint32_t(h0) | (uint32_t(h1) << 16);
+              }
+            }
+          }
+        }
+      }
     }
     __syncthreads();  // the next block overwrites the rows
   }
