@@ -52,7 +52,7 @@ constexpr int kThreads = kDecodeThreads;
 constexpr int kWaves = kThreads / 64;
 // transform stages whose records are loaded ahead (fewer for wide rows: registers)
 __host__ __device__ constexpr int ring_stages(int ppt) { return ppt >= 3 ? 4 : 8; }
-constexpr int kFusedX = 4;      // x loads per thread in the transform prologue (rows * D / 8 <= 2048)
+constexpr int kFusedPairIt = 4;  // channel pairs per thread in the transform prologue (D / 2 <= 2048)
 constexpr int kPlainX = 8;      // x loads per thread staging a plain unit (rows * D / 8 <= 4096)
 constexpr int kCUs = 256;       // MI355X compute units: one workgroup each
 constexpr size_t kLdsLimit = 144 * 1024;
@@ -99,40 +99,56 @@ __device__ inline h8 dequant_word(uint32_t u, h2 zlo, h2 zhi, uint32_t m0, uint3
 // An empty statement that makes v look redefined here: code computed from v stays below it.
 __device__ inline void pin(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
 __device__ inline void pin(float4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+__device__ inline void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 __device__ inline h8 decode_order(h8 a) { return __builtin_shufflevector(a, a, 0, 4, 1, 5, 2, 6, 3, 7); }
 
-// The transform of a unit's rows inside the kernel: x (already in registers) -> float32 rows in
-// LDS, the K stages, then x' = rows * (1/s) as float16 chunks in the decode order.
+// The transform of a unit's rows inside the kernel: x (already in registers, one 32-bit
+// channel pair per row and slot) -> float32 rows in LDS, the K stages, then x' = rows * (1/s)
+// as float16 chunks in the decode order. Both LDS passes move whole R-row channel vectors
+// with consecutive lanes on consecutive channels, so they stay (nearly) free of bank conflicts.
 template <int R, int PPT, int PD, class RP>
 __device__ inline void unit_transform(StageRing<kThreads, PPT, PD, false, true>& ring, float* rot, float* isl,
-                                      uint4* xs, const uint4 (&xv)[kFusedX], const float4 (&iv)[2], int rows, int D,
-                                      int K, int tid, RP recs) {
-  const int chunks = D / 8, xtotal = chunks * rows;
+                                      uint4* xs, const uint32_t (&xp)[kFusedPairIt][4], const float4 (&iv)[2],
+                                      int rows, int D, int K, int tid, RP recs) {
+  using V = typename RowVec<R>::T;
+  V* rv = reinterpret_cast<V*>(rot);
+  const int P = D / 2;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
     if (tid + u * kThreads < D / 4) reinterpret_cast<float4*>(isl)[tid + u * kThreads] = iv[u];
 #pragma unroll
-  for (int u = 0; u < kFusedX; ++u) {
-    const int e = tid + u * kThreads;
-    if (e < xtotal) {
-      const int m = e / chunks, c = e - m * chunks;
-      const uint32_t w[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+  for (int u = 0; u < kFusedPairIt; ++u) {
+    const int cp = tid + u * kThreads;  // channels 2 cp (low half) and 2 cp + 1
+    if (cp < P) {
+      float f0[R], f1[R];
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        rot[(c * 8 + t) * R + m] =
-            static_cast<float>(__builtin_bit_cast(_Float16, uint16_t((t & 1) ? w[t >> 1] >> 16 : w[t >> 1])));
+      for (int r = 0; r < R; ++r) {
+        f0[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(xp[u][r])));
+        f1[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(xp[u][r] >> 16)));
+      }
+      rv[2 * cp] = *reinterpret_cast<const V*>(f0);
+      rv[2 * cp + 1] = *reinterpret_cast<const V*>(f1);
     }
   }
   __syncthreads();
-  if (K > 0) ring_run_short<R>(ring, rot, K, D / 2, tid, recs);  // K <= 8; ends with a barrier
-  for (int e = tid; e < xtotal; e += kThreads) {
-    const int c = e / rows, m = e - c * rows;
-    _Float16 hv[8];
+  if (K > 0) ring_run_short<R>(ring, rot, K, P, tid, recs);  // K <= 8; ends with a barrier
+  // item j: channels e and e + 4 of 8-channel chunk c8 (e < 4) sit side by side in the decode
+  // order [0,4,1,5,2,6,3,7], i.e. one 32-bit word of each row's chunk
+  uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
+  for (int j = tid; j < P; j += kThreads) {
+    const int c8 = j >> 2, e = j & 3, ca = 8 * c8 + e;
+    const V va = rv[ca], vb = rv[ca + 4];
+    const float sa = isl[ca], sb = isl[ca + 4];
+    const float* fa = reinterpret_cast<const float*>(&va);
+    const float* fb = reinterpret_cast<const float*>(&vb);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      hv[nib_slot(t)] = static_cast<_Float16>(rot[(c * 8 + t) * R + m] * isl[c * 8 + t]);
-    xs[e] = *reinterpret_cast<const uint4*>(hv);
+    for (int m = 0; m < R; ++m)
+      if (m < rows) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fa[m] * sa));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fb[m] * sb));
+        xs32[(c8 * rows + m) * 4 + e] = lo | (hi << 16);
+      }
   }
 }
 
@@ -189,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   // ---- loads the weights must not delay (issued first, so waiting for them never waits for
   // a weight): transform records, 1/s and x, or the plain x
   StageRing<kThreads, (PPT > 0 ? PPT : 1), PD, false, true> ring;  // PPT = ceil(D/2 / 512)
-  uint4 xv[kFusedX];
+  uint32_t xp[kFusedPairIt][4];  // x channel pair tid + u * 512 of row r (rows past the unit repeat)
   float4 iv[2];
   uint4 pv[kPlainX];
   if constexpr (fused) {
@@ -201,13 +217,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
         e = e < D / 4 ? e : D / 4 - 1;
         iv[u] = __builtin_bit_cast(float4, ld16(inv_s + size_t(e) * 4));
       }
+      const gptr<const uint32_t> x32 = (gptr<const uint32_t>)ix;
 #pragma unroll
-      for (int u = 0; u < kFusedX; ++u) {
-        int e = tid + u * kThreads;
-        e = e < xtotal ? e : xtotal - 1;
-        const int m = e / chunks, c = e - m * chunks;
-        xv[u] = ld16(xg + size_t(m) * D + size_t(c) * 8);
-      }
+      for (int u = 0; u < kFusedPairIt; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // uniform guards: only the pairs and rows the unit has
+          xp[u][r] = 0u;
+          if (u * kThreads < D / 2 && r < rows) {
+            int cp = tid + u * kThreads;
+            cp = cp < D / 2 ? cp : D / 2 - 1;
+            xp[u][r] = x32[uint32_t(r) * uint32_t(D / 2) + uint32_t(cp)];
+          }
+        }
     }
   }
   const int nx = (xtotal + kThreads - 1) / kThreads;  // plain: x loads per thread (uniform)
@@ -254,7 +276,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   // the weight loads (each empty statement makes its operand look redefined at this point).
   if constexpr (fused) {
 #pragma unroll
-    for (int u = 0; u < kFusedX; ++u) pin(xv[u]);
+    for (int u = 0; u < kFusedPairIt; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pin(xp[u][r]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) pin(iv[u]);
   } else {
@@ -271,11 +295,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
       float* isl = reinterpret_cast<float*>(smem + L.isv);
       const int R = rows_class(rows);
       if (R == 1)
-        unit_transform<1>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, recs);
+        unit_transform<1>(ring, rot, isl, xs, xp, iv, rows, D, K, tid, recs);
       else if (R == 2)
-        unit_transform<2>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, recs);
+        unit_transform<2>(ring, rot, isl, xs, xp, iv, rows, D, K, tid, recs);
       else
-        unit_transform<4>(ring, rot, isl, xs, xv, iv, rows, D, K, tid, recs);
+        unit_transform<4>(ring, rot, isl, xs, xp, iv, rows, D, K, tid, recs);
     }
   }
   if constexpr (!fused) {
