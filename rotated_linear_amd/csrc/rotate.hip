@@ -2,7 +2,7 @@
 // then division by the channel scales ("ParoQuant: pairwise rotations that
 // survive deployment", section "A rotation small enough to execute").
 //
-// One workgroup of 512 threads holds R rows in LDS as float32, interleaved by
+// One workgroup of NT (512) threads holds R rows in LDS as float32, interleaved by
 // channel (lds[c * R + r]: one R-wide vector per channel, so a stage moves a pair
 // of channels for all R rows with two vector reads and two vector writes), runs
 // the K stages (rotation_core.h) and writes fp16(rows * (1/s)). Workgroups are
@@ -25,12 +25,11 @@
 namespace paro {
 namespace {
 
-constexpr int kRotThreads = 512;
 constexpr size_t kRotLds = 160 * 1024;
 constexpr int kCUs = 256;
 
-template <int R, int PPT, int PD, bool EXACT, bool PERM>
-__global__ __launch_bounds__(kRotThreads) void rotate_rows_kernel(const uint16_t* __restrict__ x,
+template <int NT, int R, int PPT, int PD, bool EXACT, bool PERM>
+__global__ __launch_bounds__(NT) void rotate_rows_kernel(const uint16_t* __restrict__ x,
                                                                    uint16_t* __restrict__ xout, int M, int D,
                                                                    int K, const PairRec* recs,
                                                                    const float* __restrict__ inv_s) {
@@ -41,7 +40,7 @@ __global__ __launch_bounds__(kRotThreads) void rotate_rows_kernel(const uint16_t
 
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
     const int row0 = blk * R;
-    StageRing<kRotThreads, PPT, PD, EXACT> ring;
+    StageRing<NT, PPT, PD, EXACT> ring;
     if (K > 0) ring_prime(ring, K, P, tid, recs);
 
     // rows -> LDS: lane = two adjacent channels (one 4-byte load per row, all of the thread's
@@ -58,13 +57,13 @@ __global__ __launch_bounds__(kRotThreads) void rotate_rows_kernel(const uint16_t
       uint32_t hv[PPT][R];  // channel pair cp = tid + u * NT: channels 2 cp (low half), 2 cp + 1
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
-        const int cp = min(tid + u * kRotThreads, P - 1);
+        const int cp = min(tid + u * NT, P - 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) hv[u][r] = xr[r][cp];
       }
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
-        const int cp = tid + u * kRotThreads;
+        const int cp = tid + u * NT;
         if (cp < P) {
           float f0[R], f1[R];
 #pragma unroll
@@ -80,36 +79,38 @@ __global__ __launch_bounds__(kRotThreads) void rotate_rows_kernel(const uint16_t
     __syncthreads();
     if (K > 0) ring_run<R>(ring, lds, K, P, tid, recs);  // ends with a barrier
 
-    // LDS -> fp16(rows * (1/s)), rows below M only; lane = channel pair as above. The thread's
-    // 1/s values are loaded together first (one memory round trip per block).
+    // LDS -> fp16(rows * (1/s)), rows below M only, one 32-bit word per row per lane: the
+    // adjacent channels (2j, 2j + 1), or with PERM channels (e, e + 4) of 8-channel chunk c8
+    // (j = 4 c8 + e), which sit side by side in the decode order. The thread's 1/s values are
+    // loaded together first (one memory round trip per block).
     {
-      // the base is made opaque per block so the loads' addresses are formed here, not hoisted
+      // the bases are made opaque per block so the loads' addresses are formed here, not hoisted
       // out of the block loop and kept live (or spilled) across the stages
       uintptr_t isb = reinterpret_cast<uintptr_t>(inv_s), ob = reinterpret_cast<uintptr_t>(xout);
       asm volatile("" : "+s"(isb), "+s"(ob));
-      float2 isv[PPT];
-#pragma unroll
-      for (int u = 0; u < PPT; ++u) isv[u] = reinterpret_cast<const float2*>(isb)[min(tid + u * kRotThreads, P - 1)];
+      const float* isp = reinterpret_cast<const float*>(isb);
+      float isa[PPT], isc[PPT];
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
-        const int cp = tid + u * kRotThreads;
-        if (cp < P) {
-          const V v0 = rows[2 * cp], v1 = rows[2 * cp + 1];
-          const float* f0 = reinterpret_cast<const float*>(&v0);
-          const float* f1 = reinterpret_cast<const float*>(&v1);
-          const int c = 2 * cp;
+        const int j = min(tid + u * NT, P - 1);
+        const int ca = PERM ? 8 * (j >> 2) + (j & 3) : 2 * j, cb = PERM ? ca + 4 : ca + 1;
+        isa[u] = isp[ca];
+        isc[u] = isp[cb];
+      }
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        const int j = tid + u * NT;
+        if (j < P) {
+          const int ca = PERM ? 8 * (j >> 2) + (j & 3) : 2 * j, cb = PERM ? ca + 4 : ca + 1;
+          const V va = rows[ca], vb = rows[cb];
+          const float* fa = reinterpret_cast<const float*>(&va);
+          const float* fb = reinterpret_cast<const float*>(&vb);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             if (row0 + r < M) {
-              const uint16_t h0 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f0[r] * isv[u].x));
-              const uint16_t h1 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f1[r] * isv[u].y));
-              uint16_t* out = reinterpret_cast<uint16_t*>(ob) + size_t(row0 + r) * D;
-              if constexpr (PERM) {  // channels c, c + 1 sit apart in the decode order
-                out[(c & ~7) | nib_slot(c & 7)] = h0;
-                out[(c & ~7) | nib_slot((c + 1) & 7)] = h1;
-              } else {
-                reinterpret_cast<uint32_t*>(out)[cp] = uint32_t(h0) | (uint32_t(h1) << 16);
-              }
+              const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fa[r] * isa[u]));
+              const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fb[r] * isc[u]));
+              reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(ob) + size_t(row0 + r) * D)[j] = lo | (hi << 16);
             }
           }
         }
@@ -119,10 +120,10 @@ __global__ __launch_bounds__(kRotThreads) void rotate_rows_kernel(const uint16_t
   }
 }
 
-template <int R, int PPT, int PD, bool EXACT, bool PERM>
+template <int NT, int R, int PPT, int PD, bool EXACT, bool PERM>
 hipError_t launch_rows(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
   const size_t lds = size_t(Rt.D) * R * sizeof(float);
-  const void* fn = reinterpret_cast<const void*>(&rotate_rows_kernel<R, PPT, PD, EXACT, PERM>);
+  const void* fn = reinterpret_cast<const void*>(&rotate_rows_kernel<NT, R, PPT, PD, EXACT, PERM>);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
@@ -130,36 +131,33 @@ hipError_t launch_rows(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xou
   const long nblk = (M + R - 1) / R;
   const long per_cu = std::max<long>(1, long(kRotLds / lds));  // workgroups one CU holds at once
   const int grid = int(std::min<long>(nblk, per_cu * kCUs));
-  hipLaunchKernelGGL((rotate_rows_kernel<R, PPT, PD, EXACT, PERM>), dim3(grid), dim3(kRotThreads), lds, st, x,
-                     xout, M, Rt.D, Rt.K, Rt.rec, Rt.inv_s);
+  hipLaunchKernelGGL((rotate_rows_kernel<NT, R, PPT, PD, EXACT, PERM>), dim3(grid), dim3(NT), lds, st, x, xout, M,
+                     Rt.D, Rt.K, Rt.rec, Rt.inv_s);
   return hipGetLastError();
 }
 
-template <int R, int PPT, int PD, bool PERM>
+template <int NT, int R, int PPT, int PD, bool PERM>
 hipError_t launch_exact(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  if (Rt.D / 2 == PPT * kRotThreads) return launch_rows<R, PPT, PD, true, PERM>(Rt, M, x, xout, st);
-  return launch_rows<R, PPT, PD, false, PERM>(Rt, M, x, xout, st);
+  if (Rt.D / 2 == PPT * NT) return launch_rows<NT, R, PPT, PD, true, PERM>(Rt, M, x, xout, st);
+  return launch_rows<NT, R, PPT, PD, false, PERM>(Rt, M, x, xout, st);
 }
 
-// Pairs per thread per stage (PPT) and its ring depth; R rows take PPT up to kMaxPpt<R>
-// (beyond it the float32 rows and the records outgrow the registers).
-template <int R>
-constexpr int kMaxPpt = R == 4 ? 9 : 16;
-
+// Threads, pairs per thread per stage (PPT) and ring depth by row width (the ring is shallower
+// for wide rows, whose records and row vectors take more registers).
 template <int R, bool PERM>
 hipError_t launch_ppt(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  const int ppt = (Rt.D / 2 + kRotThreads - 1) / kRotThreads;
-  if (ppt <= 1) return launch_exact<R, 1, 8, PERM>(Rt, M, x, xout, st);
-  if (ppt <= 2) return launch_exact<R, 2, 8, PERM>(Rt, M, x, xout, st);
-  if (ppt <= 3) return launch_exact<R, 3, 4, PERM>(Rt, M, x, xout, st);
-  if (ppt <= 4) return launch_exact<R, 4, 4, PERM>(Rt, M, x, xout, st);
-  if (ppt <= 6) return launch_exact<R, 6, 2, PERM>(Rt, M, x, xout, st);
-  if (ppt <= 9) return launch_exact<R, 9, 2, PERM>(Rt, M, x, xout, st);
-  if constexpr (kMaxPpt<R> >= 12)
-    if (ppt <= 12) return launch_exact<R, 12, 2, PERM>(Rt, M, x, xout, st);
-  if constexpr (kMaxPpt<R> >= 14)
-    if (ppt <= 14) return launch_exact<R, 14, 1, PERM>(Rt, M, x, xout, st);
-  if constexpr (kMaxPpt<R> >= 16) return launch_exact<R, 16, 1, PERM>(Rt, M, x, xout, st);
+  const int P = Rt.D / 2;
+  if (P <= 512) return launch_exact<512, R, 1, 8, PERM>(Rt, M, x, xout, st);
+  if (P <= 1024) return launch_exact<512, R, 2, 8, PERM>(Rt, M, x, xout, st);
+  if (P <= 1536) return launch_exact<512, R, 3, 4, PERM>(Rt, M, x, xout, st);
+  if (P <= 2048) return launch_exact<512, R, 4, 4, PERM>(Rt, M, x, xout, st);
+  if (P <= 3072) return launch_exact<512, R, 6, 2, PERM>(Rt, M, x, xout, st);
+  if (P <= 4608) return launch_exact<512, R, 9, 2, PERM>(Rt, M, x, xout, st);
+  if constexpr (R <= 2) {  // wider rows (D > 9216) never take 4 rows per workgroup
+    if (P <= 6144) return launch_exact<512, R, 12, 2, PERM>(Rt, M, x, xout, st);
+    if (P <= 7168) return launch_exact<512, R, 14, 1, PERM>(Rt, M, x, xout, st);
+    return launch_exact<512, R, 16, 1, PERM>(Rt, M, x, xout, st);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -168,9 +166,8 @@ hipError_t launch_r(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, h
   // Rows per workgroup: a stage's parameters are read once per block, so larger blocks
   // save their traffic once there are enough rows to give every CU a block.
   const size_t row_bytes = size_t(R.D) * 4;
-  const int ppt = (R.D / 2 + kRotThreads - 1) / kRotThreads;
-  if (M >= 4 * kCUs && 4 * row_bytes <= kRotLds && ppt <= kMaxPpt<4>) return launch_ppt<4, PERM>(R, M, x, xout, st);
-  if (M >= 2 * kCUs && 2 * row_bytes <= kRotLds && ppt <= kMaxPpt<2>) return launch_ppt<2, PERM>(R, M, x, xout, st);
+  if (M >= 4 * kCUs && 4 * row_bytes <= kRotLds && R.D <= 9216) return launch_ppt<4, PERM>(R, M, x, xout, st);
+  if (M >= 2 * kCUs && 2 * row_bytes <= kRotLds) return launch_ppt<2, PERM>(R, M, x, xout, st);
   return launch_ppt<1, PERM>(R, M, x, xout, st);
 }
 
@@ -178,7 +175,7 @@ hipError_t launch_r(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, h
 
 hipError_t launch_rotate(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, bool nibble_order,
                          hipStream_t st) {
-  if (R.D / 2 > 16 * kRotThreads) return hipErrorInvalidValue;
+  if (R.D / 2 > 8 * 1024) return hipErrorInvalidValue;
   return nibble_order ? launch_r<true>(R, M, x, xout, st) : launch_r<false>(R, M, x, xout, st);
 }
 
