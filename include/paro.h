@@ -153,9 +153,11 @@ paro_status paro_pack_weights(const paro_rotation* r, int N, const void* W, uint
 paro_status paro_rotate(const paro_rotation* r, int M, const void* x, void* xout, void* stream);
 
 /* Workspace bytes that suffice for paro_w4a16_linear / paro_rotated_linear at
- * (M, D, N) with any transform: M * D * 2 rounded up to 256 (0 for M <= 0 or an
- * invalid D). Calls whose transform runs inside the decode kernel (M <= 16,
- * D <= 4096, K <= 8) and plain linears use none of it and accept ws == NULL. */
+ * (M, D, N) with any transform (0 for M <= 0 or an invalid D): M * D * 2 rounded
+ * up to 256 for the transformed x, plus, for prefill-shaped calls (M > 16), room
+ * for the float32 partial sums [S][M][N] of a GEMM whose reduction over D is
+ * split S ways to fill the GPU. Calls whose transform runs inside the decode
+ * kernel (M <= 16, D <= 4096, K <= 8) use none of it and accept ws == NULL. */
 size_t paro_workspace_bytes(int M, int D, int N);
 
 /*
@@ -164,8 +166,11 @@ size_t paro_workspace_bytes(int M, int D, int N);
  * layer): y[m][n] = sum_g scale[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g]),
  * products of float16 values exact, accumulation in float32, y stored as
  * ydtype (PARO_F16 rounds once). x float16 [M][D]; y [M][N] must not overlap
- * any input. ws is a device buffer of ws_bytes >= paro_workspace_bytes(M, D, N)
- * (may be NULL when that is 0).
+ * any input. ws is an optional device buffer: given at least
+ * paro_workspace_bytes(M, D, N) bytes (which must not overlap any operand), a
+ * prefill-shaped call may split its reduction over D and keep the partial sums
+ * there; with less (or NULL) it does not split. The two differ only in float32
+ * summation order; each is deterministic.
  */
 paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t* qweight,
                               const void* scales, const void* zeros, void* y, int ydtype, void* ws,
@@ -177,9 +182,10 @@ paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t*
  * operand) immediately followed by the INT4 linear of paro_w4a16_linear, with
  * the weights packed by paro_pack_weights for the same transform. With M <= 16,
  * D <= 4096 and K <= 8 the transform runs inside the decode kernel (one launch,
- * no workspace); otherwise a transform kernel writes x' into ws (at least
- * M * D * 2 bytes, else PARO_EWORKSPACE) and the linear reads it, on `stream`.
- * Arguments as in paro_w4a16_linear, with D = r->D.
+ * no workspace); otherwise a transform kernel writes x' into ws, which must
+ * then hold at least paro_workspace_bytes(M, D, N) bytes (else
+ * PARO_EWORKSPACE; the rest of it serves the linear as above), and the linear
+ * reads it, on `stream`. Arguments as in paro_w4a16_linear, with D = r->D.
  */
 paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void* x,
                                 const uint8_t* qweight, const void* scales, const void* zeros,
