@@ -169,6 +169,17 @@ def time_graphs(torch, graphs, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def time_slots(torch, fn, n_slots, per, steps, warmup):
+    """fn(slot) for slot < n_slots, captured as graphs of `per` consecutive slots (so one replay
+    carries several steps and host launch cost stays out of the per-step time); returns ms per
+    step over `steps` steps after `warmup` untimed ones."""
+    n_graphs = max(1, n_slots // per)
+    gs = capture(torch, lambda g: [fn(g * per + r) for r in range(per)], n_graphs)
+    ms = time_graphs(torch, gs, max(1, steps // per), max(1, warmup // per)) / per
+    del gs
+    return ms
+
+
 # --------------------------------------------------------------------------- #
 # CPU oracle baseline
 # --------------------------------------------------------------------------- #
@@ -233,11 +244,8 @@ def main():
     n_graphs = max(1, n_slots // per_graph)
 
     def timed(rotated, batched):
-        gs = capture(torch, lambda g: [step.enqueue(g * per_graph + r, rotated=rotated, batched=batched)
-                                       for r in range(per_graph)], n_graphs)
-        ms = time_graphs(torch, gs, args.steps // per_graph, max(1, args.warmup // per_graph)) / per_graph
-        del gs
-        return ms
+        return time_slots(torch, lambda s: step.enqueue(s, rotated=rotated, batched=batched), n_graphs * per_graph,
+                          per_graph, args.steps, args.warmup)
 
     # the step: the 12 projections as one batched call (one launch of the decode kernel)
     ms_rot = timed(True, True)
@@ -343,34 +351,71 @@ def traffic_run(rl, torch, W, reps):
 
 
 def extras(rl, torch, W, args):
-    """Larger shapes: gate+up decode (HBM) and down_proj prefill (MFMA), rotated vs plain."""
+    """Larger shapes, rotated vs plain: gate+up decode (HBM) and prefill at M = 256 (MFMA), down_proj
+    prefill (MFMA), and the 8B-class layer at decode M = 64 and prefill M = 4096."""
     res = {}
     L3 = Linear(rl, torch, W.make_linear(3, 0))
     n3 = max(4, math.ceil(POOL_BYTES / L3.set_bytes()))
     L3.make_copies(rl, n3)
     for M in (1, 16):
         st = Step(rl, torch, [L3], [M])
-        gr = capture(torch, lambda s: st.enqueue(s), n3)
-        ms_r = time_graphs(torch, gr, max(20, args.steps // 2), 5)
-        gp = capture(torch, lambda s: st.enqueue(s, rotated=False), n3)
-        ms_p = time_graphs(torch, gp, max(20, args.steps // 2), 5)
+        ms_r = time_slots(torch, lambda s: st.enqueue(s), n3, 8, 2 * n3, 16)
+        ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), n3, 8, 2 * n3, 16)
         res[f"gate_up_decode_M{M}"] = {"GB/s": round(st.bytes() / (ms_r * 1e-3) / 1e9, 2),
                                        "frac_hbm": round(st.bytes() / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                        "us": round(ms_r * 1e3, 3),
                                        "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
-        del gr, gp
     L3.copies = []
+    st = Step(rl, torch, [L3], [256])  # gate+up at M = 256: MFMA-bound
+    ms_r = time_slots(torch, lambda s: st.enqueue(s), 4, 4, 20, 4)
+    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), 4, 4, 20, 4)
+    tf = st.flops() / (ms_r * 1e-3) / 1e12
+    res["gate_up_prefill_M256"] = {"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                   "us": round(ms_r * 1e3, 2),
+                                   "plain_TFLOP/s": round(st.flops() / (ms_p * 1e-3) / 1e12, 2),
+                                   "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
+    del st, L3
     L4 = Linear(rl, torch, W.make_linear(4, 0))
     st = Step(rl, torch, [L4], [2048])
-    gr = capture(torch, lambda s: st.enqueue(s), 1)
-    ms_r = time_graphs(torch, gr, 20, 3)
-    gp = capture(torch, lambda s: st.enqueue(s, rotated=False), 1)
-    ms_p = time_graphs(torch, gp, 20, 3)
+    ms_r = time_slots(torch, lambda s: st.enqueue(s), 4, 4, 20, 4)
+    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), 4, 4, 20, 4)
     tf = st.flops() / (ms_r * 1e-3) / 1e12
     res["down_prefill_M2048"] = {"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                  "us": round(ms_r * 1e3, 2),
                                  "plain_TFLOP/s": round(st.flops() / (ms_p * 1e-3) / 1e12, 2),
                                  "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
+    del st, L4
+    res.update(layer8b(rl, torch, W, args))
+    return res
+
+
+def layer8b(rl, torch, W, args):
+    """The 8B-class decoder layer (7 linears, each with its own transform): decode at M = 64 as one
+    batched call over a cold pool (HBM-bound), and prefill at M = 4096 (MFMA-bound)."""
+    res = {}
+    lins = [Linear(rl, torch, W.make_linear(5, i)) for i in range(len(W.WORKLOADS[5].linears))]
+    set_bytes = sum(l.set_bytes() for l in lins)
+    n_sets = max(2, math.ceil(0.6 * POOL_BYTES / set_bytes))  # about 2.5 times the Infinity Cache
+    for l in lins:
+        l.make_copies(rl, n_sets)
+    st = Step(rl, torch, lins, [64])
+    ms_r = time_slots(torch, lambda s: st.enqueue(s, batched=True), n_sets, 2, 4 * n_sets, n_sets)
+    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False, batched=True), n_sets, 2, 4 * n_sets, n_sets)
+    gbs = st.bytes() / (ms_r * 1e-3) / 1e9
+    res["layer8b_decode_M64"] = {"GB/s": round(gbs, 2), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                 "us": round(ms_r * 1e3, 2), "algorithmic_bytes": st.bytes(),
+                                 "plain_us": round(ms_p * 1e3, 2),
+                                 "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
+    for l in lins:
+        l.copies = []
+    st = Step(rl, torch, lins, [4096])
+    ms_r = time_slots(torch, lambda s: st.enqueue(s, batched=True), 2, 2, 6, 2)
+    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False, batched=True), 2, 2, 6, 2)
+    tf = st.flops() / (ms_r * 1e-3) / 1e12
+    res["layer8b_prefill_M4096"] = {"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                    "us": round(ms_r * 1e3, 2),
+                                    "plain_TFLOP/s": round(st.flops() / (ms_p * 1e-3) / 1e12, 2),
+                                    "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
     return res
 
 

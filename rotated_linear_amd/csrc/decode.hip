@@ -24,8 +24,9 @@
 //    in LDS chunk-major ([D/8][rows] 16-byte chunks). When a wave has at most 4 groups per
 //    tile it keeps its A fragments in registers for the whole kernel; lanes feeding rows past
 //    the unit's rows read a zero chunk;
-//  * a unit with a transform loads its stage records, x and 1/s ahead of the weights and runs
-//    the K stages in LDS (rotation_core.h) while the weight ring is in flight;
+//  * a unit with a transform loads x, 1/s and its stage records, writes its rows to LDS, and
+//    only then issues the weight ring, which lands while the K stages run in LDS
+//    (rotation_core.h);
 //  * per-tile partial sums go to LDS and the WPT waves are combined after the loop, so the
 //    loop holds no barrier and no global store.
 #include <string.h>
@@ -103,14 +104,14 @@ __device__ inline void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 __device__ inline h8 decode_order(h8 a) { return __builtin_shufflevector(a, a, 0, 4, 1, 5, 2, 6, 3, 7); }
 
-// The transform of a unit's rows inside the kernel: x (already in registers, one 32-bit
-// channel pair per row and slot) -> float32 rows in LDS, the K stages, then x' = rows * (1/s)
-// as float16 chunks in the decode order. Both LDS passes move whole R-row channel vectors
-// with consecutive lanes on consecutive channels, so they stay (nearly) free of bank conflicts.
-template <int R, int PPT, int PD, class RP>
-__device__ inline void unit_transform(StageRing<kThreads, PPT, PD, false, true>& ring, float* rot, float* isl,
-                                      uint4* xs, const uint32_t (&xp)[kFusedPairIt][4], const float4 (&iv)[2],
-                                      int rows, int D, int K, int tid, RP recs) {
+// The transform of a unit's rows inside the kernel, in two steps. unit_fill: x (already in
+// registers, one 32-bit channel pair per row and slot) -> float32 rows in LDS, and 1/s -> LDS.
+// unit_finish: the K stages, then x' = rows * (1/s) as float16 chunks in the decode order. Both
+// LDS passes move whole R-row channel vectors with consecutive lanes on consecutive channels,
+// so they stay (nearly) free of bank conflicts.
+template <int R>
+__device__ inline void unit_fill(float* rot, float* isl, const uint32_t (&xp)[kFusedPairIt][4],
+                                 const float4 (&iv)[2], int D, int tid) {
   using V = typename RowVec<R>::T;
   V* rv = reinterpret_cast<V*>(rot);
   const int P = D / 2;
@@ -131,6 +132,14 @@ __device__ inline void unit_transform(StageRing<kThreads, PPT, PD, false, true>&
       rv[2 * cp + 1] = *reinterpret_cast<const V*>(f1);
     }
   }
+}
+
+template <int R, int PPT, int PD, class RP>
+__device__ inline void unit_finish(StageRing<kThreads, PPT, PD, false, true>& ring, float* rot, const float* isl,
+                                   uint4* xs, int rows, int D, int K, int tid, RP recs) {
+  using V = typename RowVec<R>::T;
+  V* rv = reinterpret_cast<V*>(rot);
+  const int P = D / 2;
   __syncthreads();
   if (K > 0) ring_run_short<R>(ring, rot, K, P, tid, recs);  // K <= 8; ends with a barrier
   // item j: channels e and e + 4 of 8-channel chunk c8 (e < 4) sit side by side in the decode
@@ -203,20 +212,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   if (tid == 0) xs[zero_idx] = uint4{0u, 0u, 0u, 0u};
 
   // ---- loads the weights must not delay (issued first, so waiting for them never waits for
-  // a weight): transform records, 1/s and x, or the plain x
+  // a weight): x, 1/s and the transform records, or the plain x
   StageRing<kThreads, (PPT > 0 ? PPT : 1), PD, false, true> ring;  // PPT = ceil(D/2 / 512)
   uint32_t xp[kFusedPairIt][4];  // x channel pair tid + u * 512 of row r (rows past the unit repeat)
   float4 iv[2];
   uint4 pv[kPlainX];
   if constexpr (fused) {
     {
-      ring_prime(ring, K, D / 2, tid, recs);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        int e = tid + u * kThreads;
-        e = e < D / 4 ? e : D / 4 - 1;
-        iv[u] = __builtin_bit_cast(float4, ld16(inv_s + size_t(e) * 4));
-      }
+      // x and 1/s first: filling the rows waits for them only (loads complete in issue order),
+      // while the stage records behind them are needed one stage at a time
       const gptr<const uint32_t> x32 = (gptr<const uint32_t>)ix;
 #pragma unroll
       for (int u = 0; u < kFusedPairIt; ++u)
@@ -230,6 +234,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
             xp[u][r] = x32[uint32_t(r) * uint32_t(D / 2) + uint32_t(cp)];
           }
         }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        int e = tid + u * kThreads;
+        e = e < D / 4 ? e : D / 4 - 1;
+        iv[u] = __builtin_bit_cast(float4, ld16(inv_s + size_t(e) * 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      ring_prime(ring, K, D / 2, tid, recs);
     }
   }
   const int nx = (xtotal + kThreads - 1) / kThreads;  // plain: x loads per thread (uniform)
@@ -243,6 +255,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
         pv[u] = ld16(xg + size_t(m) * D + size_t(c) * 8);
       }
     }
+  }
+
+  // With the transform inside, the rows go to LDS before any weight load is issued: x is then
+  // the only traffic in flight and arrives with the memory system's idle latency, while the
+  // weights issued next land during the stages.
+  float* const rot = reinterpret_cast<float*>(smem + L.rot);
+  float* const isl = reinterpret_cast<float*>(smem + L.isv);
+  if constexpr (fused) {
+    const int R = rows_class(rows);
+    if (R == 1)
+      unit_fill<1>(rot, isl, xp, iv, D, tid);
+    else if (R == 2)
+      unit_fill<2>(rot, isl, xp, iv, D, tid);
+    else
+      unit_fill<4>(rot, isl, xp, iv, D, tid);
   }
 
   // ---- weight ring prologue: the first PF groups of this wave (nothing may move across it:
@@ -272,16 +299,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
     // keep the refill order (weights, scale, zero per group): the loop's wait counts assume it
     __builtin_amdgcn_sched_barrier(0);
   }
-  // The staged values are first used here: nothing computed from them may be hoisted above
-  // the weight loads (each empty statement makes its operand look redefined at this point).
-  if constexpr (fused) {
-#pragma unroll
-    for (int u = 0; u < kFusedPairIt; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pin(xp[u][r]);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) pin(iv[u]);
-  } else {
+  // Plain units: the staged x is first used here, so nothing computed from it may be hoisted
+  // above the weight loads (each empty statement makes its operand look redefined here).
+  if constexpr (!fused) {
 #pragma unroll
     for (int u = 0; u < kPlainX; ++u)
       if (u < nx) pin(pv[u]);
@@ -290,17 +310,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
 
   // ---- stage the A operand
   if constexpr (fused) {
-    {
-      float* rot = reinterpret_cast<float*>(smem + L.rot);
-      float* isl = reinterpret_cast<float*>(smem + L.isv);
-      const int R = rows_class(rows);
-      if (R == 1)
-        unit_transform<1>(ring, rot, isl, xs, xp, iv, rows, D, K, tid, recs);
-      else if (R == 2)
-        unit_transform<2>(ring, rot, isl, xs, xp, iv, rows, D, K, tid, recs);
-      else
-        unit_transform<4>(ring, rot, isl, xs, xp, iv, rows, D, K, tid, recs);
-    }
+    const int R = rows_class(rows);
+    if (R == 1)
+      unit_finish<1>(ring, rot, isl, xs, rows, D, K, tid, recs);
+    else if (R == 2)
+      unit_finish<2>(ring, rot, isl, xs, rows, D, K, tid, recs);
+    else
+      unit_finish<4>(ring, rot, isl, xs, rows, D, K, tid, recs);
   }
   if constexpr (!fused) {
     const bool perm = !xperm;

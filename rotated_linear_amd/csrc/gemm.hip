@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs p) {
   // barrier per stage. Step t computes stage t from LDS buffer t % 2 after issuing the loads of
   // stage t + PD into the register stage that held stage t, then moves stage t + 1 from its
   // registers into the other buffer: a load has PD stage computations to arrive.
-  constexpr int U = PD == 3 ? 6 : 2;  // steps per loop iteration: static register/buffer indices
+  constexpr int U = PD == 3 ? 6 : (PD == 4 ? 4 : 2);  // steps per iteration: static register/buffer indices
   Stage<T> reg[PD];
 #pragma unroll
   for (int i = 0; i < PD; ++i) load(reg[i], i);
@@ -428,6 +428,7 @@ hipError_t launch_block(int M, int D, int N, const uint16_t* x, bool x_nibble_or
   PARO_GEMM_CASE(64, 256, 2, 2)
   PARO_GEMM_CASE(64, 192, 2, 2)
   PARO_GEMM_CASE(64, 128, 2, 2)
+  PARO_GEMM_CASE(64, 128, 2, 4)
 #undef PARO_GEMM_CASE
   if (e != hipSuccess || g.splits == 1) return e;
   const size_t count = size_t(M) * N;
