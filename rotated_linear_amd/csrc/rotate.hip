@@ -6,14 +6,19 @@
 // channel (lds[c * R + r]: one R-wide vector per channel, so a stage moves a pair
 // of channels for all R rows with two vector reads and two vector writes), runs
 // the K stages (rotation_core.h) and writes fp16(rows * (1/s)). Workgroups are
-// persistent over blocks of R rows. Stage parameters stream through a register
-// ring issued before the block's rows are loaded.
+// persistent over blocks of R rows and software-pipelined across them: the next
+// block's rows are loaded into registers while the current block's stages run,
+// and the current block's output is stored from registers after the next block
+// has been placed in LDS, so the global traffic overlaps the LDS-bound stages.
+// Stage parameters stream through a register ring.
 //
-// LDS banks (32 on gfx950): inside a stage, the host's pair order keeps the channels
-// of 8 (16, 32) consecutive lanes distinct modulo 8 (16, 32), so the R = 4 (2, 1)
-// vector accesses are conflict-free. Rows move between global memory and LDS two
-// adjacent channels per lane (4-byte accesses, every load of a block in flight at
-// once), so a wave's vector accesses cover consecutive channels.
+// LDS banks: measured on gfx950, a wave's 16-byte (8-byte, 4-byte) accesses run at
+// full rate when every aligned run of 16 (32, 64) consecutive lanes touches
+// channels that are distinct modulo 16 (32, 64). Inside a stage the host's pair
+// order gives exactly that for the R = 4 (2, 1) vectors (runs of 64, 32, 16 and 8
+// pairs with distinct residues modulo their length). Rows move between global
+// memory and LDS two adjacent channels per lane, so a wave's vector accesses
+// cover consecutive channels.
 //
 // With PERM the output keeps every 8-channel word in the order the INT4 decode of
 // the linear kernels produces ([0,4,1,5,2,6,3,7]), which is how
@@ -28,6 +33,15 @@ namespace {
 constexpr size_t kRotLds = 160 * 1024;
 constexpr int kCUs = 256;
 
+// The thread index, made opaque at the point of use: per-lane addresses computed from it are
+// formed where they are used instead of being hoisted out of the block loop as invariants
+// and kept live (or spilled) across the stages.
+__device__ inline int fresh_tid() {
+  int t = int(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 template <int NT, int R, int PPT, int PD, bool EXACT, bool PERM>
 __global__ __launch_bounds__(NT) void rotate_rows_kernel(const uint16_t* __restrict__ x,
                                                                    uint16_t* __restrict__ xout, int M, int D,
@@ -36,87 +50,122 @@ __global__ __launch_bounds__(NT) void rotate_rows_kernel(const uint16_t* __restr
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [D][R]
   const int tid = threadIdx.x;
   const int P = D / 2;
-  const int nblk = (M + R - 1) / R;
+  const int nblk = (M + R - 1) / R;  // the grid never exceeds it
+  using V = typename RowVec<R>::T;
+  V* rows = reinterpret_cast<V*>(lds);
 
-  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    const int row0 = blk * R;
-    StageRing<NT, PPT, PD, EXACT> ring;
-    if (K > 0) ring_prime(ring, K, P, tid, recs);
+  // Output item j of a thread (j = tid + u * NT): the adjacent channels (2j, 2j + 1), or with
+  // PERM channels (e, e + 4) of 8-channel chunk c8 (j = 4 c8 + e), which sit side by side in the
+  // decode order: one 32-bit word per row. Its two 1/s values are the same for every block:
+  // narrow rows keep them in registers for the whole kernel, wide rows (whose registers are
+  // taken by the stage ring and the next block's rows) reload them per block.
+  constexpr bool kHoldS = PPT <= 6;
+  float isa[PPT], isc[PPT];
+  auto load_s = [&]() {
+    const int tl = fresh_tid();
+    uintptr_t isb = reinterpret_cast<uintptr_t>(inv_s);
+    asm volatile("" : "+s"(isb));
+    const gptr<const float> isp = (gptr<const float>)isb;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int j = min(tl + u * NT, P - 1);
+      const int ca = PERM ? 8 * (j >> 2) + (j & 3) : 2 * j, cb = PERM ? ca + 4 : ca + 1;
+      isa[u] = isp[ca];
+      isc[u] = isp[cb];
+    }
+  };
+  if constexpr (kHoldS) load_s();
 
-    // rows -> LDS: lane = two adjacent channels (one 4-byte load per row, all of the thread's
-    // loads in flight at once); a wave writes 128 consecutive channel vectors
-    using V = typename RowVec<R>::T;
-    V* rows = reinterpret_cast<V*>(lds);
+  // The rows of a block travel through registers, two adjacent channels per lane and row (one
+  // 4-byte access each; a wave covers 128 consecutive channels). Pointers are typed as global
+  // memory (not generic), so the accesses are global_* and an LDS wait or barrier never waits
+  // for them; the bases are made opaque where the accesses issue, so their addresses are
+  // formed there and not kept live (or spilled) across the stages.
+  uint32_t hv[PPT][R];
+  auto load_rows = [&](int b) {
+    const int tl = fresh_tid();
     uintptr_t xb = reinterpret_cast<uintptr_t>(x);
-    asm volatile("" : "+s"(xb));  // as for 1/s below: addresses formed where the loads issue
-    const uint32_t* xr[R];
+    asm volatile("" : "+s"(xb));
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      xr[r] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(xb) + size_t(min(row0 + r, M - 1)) * D);
-    {
-      uint32_t hv[PPT][R];  // channel pair cp = tid + u * NT: channels 2 cp (low half), 2 cp + 1
+    for (int r = 0; r < R; ++r) {
+      const gptr<const uint32_t> xr = (gptr<const uint32_t>)(xb + size_t(min(b * R + r, M - 1)) * D * sizeof(uint16_t));
 #pragma unroll
-      for (int u = 0; u < PPT; ++u) {
-        const int cp = min(tid + u * NT, P - 1);
+      for (int u = 0; u < PPT; ++u) hv[u][r] = xr[min(tl + u * NT, P - 1)];
+    }
+  };
+  auto fill = [&]() {
+    const int tl = fresh_tid();
 #pragma unroll
-        for (int r = 0; r < R; ++r) hv[u][r] = xr[r][cp];
-      }
+    for (int u = 0; u < PPT; ++u) {
+      const int cp = tl + u * NT;  // channels 2 cp (low half) and 2 cp + 1
+      if (cp < P) {
+        float f0[R], f1[R];
 #pragma unroll
-      for (int u = 0; u < PPT; ++u) {
-        const int cp = tid + u * NT;
-        if (cp < P) {
-          float f0[R], f1[R];
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            f0[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r])));
-            f1[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r] >> 16)));
-          }
-          rows[2 * cp] = *reinterpret_cast<const V*>(f0);
-          rows[2 * cp + 1] = *reinterpret_cast<const V*>(f1);
+        for (int r = 0; r < R; ++r) {
+          f0[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r])));
+          f1[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r] >> 16)));
         }
+        rows[2 * cp] = *reinterpret_cast<const V*>(f0);
+        rows[2 * cp + 1] = *reinterpret_cast<const V*>(f1);
       }
     }
-    __syncthreads();
+  };
+
+  // Software pipeline over the workgroup's blocks of R rows: the next block's rows are loaded
+  // while this block's stages run, and this block's output leaves from registers while the
+  // next block's stages run, so global traffic overlaps the LDS-bound stages.
+  int blk = blockIdx.x;
+  load_rows(blk);
+  StageRing<NT, PPT, PD, EXACT> ring;
+  if (K > 0) ring_prime(ring, K, P, tid, recs);
+  fill();
+  __syncthreads();
+  for (;;) {
+    const int next = blk + int(gridDim.x);
+    const bool more = next < nblk;  // uniform
+    if (more) load_rows(next);
     if (K > 0) ring_run<R>(ring, lds, K, P, tid, recs);  // ends with a barrier
 
-    // LDS -> fp16(rows * (1/s)), rows below M only, one 32-bit word per row per lane: the
-    // adjacent channels (2j, 2j + 1), or with PERM channels (e, e + 4) of 8-channel chunk c8
-    // (j = 4 c8 + e), which sit side by side in the decode order. The thread's 1/s values are
-    // loaded together first (one memory round trip per block).
-    {
-      // the bases are made opaque per block so the loads' addresses are formed here, not hoisted
-      // out of the block loop and kept live (or spilled) across the stages
-      uintptr_t isb = reinterpret_cast<uintptr_t>(inv_s), ob = reinterpret_cast<uintptr_t>(xout);
-      asm volatile("" : "+s"(isb), "+s"(ob));
-      const float* isp = reinterpret_cast<const float*>(isb);
-      float isa[PPT], isc[PPT];
+    // LDS -> fp16(rows * (1/s)) packed in registers
+    if constexpr (!kHoldS) load_s();
+    uint32_t ov[PPT][R];
+    const int to = fresh_tid();
 #pragma unroll
-      for (int u = 0; u < PPT; ++u) {
-        const int j = min(tid + u * NT, P - 1);
-        const int ca = PERM ? 8 * (j >> 2) + (j & 3) : 2 * j, cb = PERM ? ca + 4 : ca + 1;
-        isa[u] = isp[ca];
-        isc[u] = isp[cb];
+    for (int u = 0; u < PPT; ++u) {
+      const int j = min(to + u * NT, P - 1);
+      const int ca = PERM ? 8 * (j >> 2) + (j & 3) : 2 * j, cb = PERM ? ca + 4 : ca + 1;
+      const V va = rows[ca], vb = rows[cb];
+      const float* fa = reinterpret_cast<const float*>(&va);
+      const float* fb = reinterpret_cast<const float*>(&vb);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fa[r] * isa[u]));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fb[r] * isc[u]));
+        ov[u][r] = lo | (hi << 16);
       }
+    }
+    __syncthreads();  // every read of this block's rows is done
+    if (more) {
+      if (K > 0) ring_prime(ring, K, P, tid, recs);
+      fill();
+    }
+    {
+      const int ts = fresh_tid();
+      uintptr_t ob = reinterpret_cast<uintptr_t>(xout);
+      asm volatile("" : "+s"(ob));
 #pragma unroll
-      for (int u = 0; u < PPT; ++u) {
-        const int j = tid + u * NT;
-        if (j < P) {
-          const int ca = PERM ? 8 * (j >> 2) + (j & 3) : 2 * j, cb = PERM ? ca + 4 : ca + 1;
-          const V va = rows[ca], vb = rows[cb];
-          const float* fa = reinterpret_cast<const float*>(&va);
-          const float* fb = reinterpret_cast<const float*>(&vb);
+      for (int r = 0; r < R; ++r) {
+        if (blk * R + r < M) {
+          const gptr<uint32_t> orow = (gptr<uint32_t>)(ob + size_t(blk * R + r) * D * sizeof(uint16_t));
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if (row0 + r < M) {
-              const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fa[r] * isa[u]));
-              const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fb[r] * isc[u]));
-              reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(ob) + size_t(row0 + r) * D)[j] = lo | (hi << 16);
-            }
-          }
+          for (int u = 0; u < PPT; ++u)
+            if (ts + u * NT < P) orow[ts + u * NT] = ov[u][r];
         }
       }
     }
-    __syncthreads();  // the next block overwrites the rows
+    if (!more) break;
+    __syncthreads();  // the next block's rows are in LDS
+    blk = next;
   }
 }
 

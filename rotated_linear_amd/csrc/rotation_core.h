@@ -64,26 +64,35 @@ struct StageRing {
     }
   }
 
-  // All of the thread's gathers first, then all updates: the pairs of a stage are disjoint,
-  // but the compiler cannot know that, so interleaving reads and writes per pair would
-  // serialize every pair behind the previous pair's LDS round trip. Gathers are unconditional
-  // (a slot past the stage holds the clamped record of pair P - 1, whose values it then
-  // ignores); updates are guarded (with TIGHT, only the last slot's).
+  // The thread's gathers first, then the updates, in batches of up to 16 / R pairs: the pairs of
+  // a stage are disjoint, but the compiler cannot know that, so interleaving reads and writes
+  // per pair would serialize every pair behind the previous pair's LDS round trip, while one
+  // batch of all PPT pairs would hold 2 * PPT * R gathered floats in registers at once (wide
+  // rows then spill). Gathers are unconditional (a slot past the stage holds the clamped record
+  // of pair P - 1, whose values it then ignores); updates are guarded (with TIGHT, only the last
+  // slot's).
   template <int R, int slot>
   __device__ inline void apply(typename RowVec<R>::T* rows, int P, int tid) const {
     using V = typename RowVec<R>::T;
-    V vi[PPT], vj[PPT];
+    constexpr int B = (16 / R) < PPT ? (16 / R) : PPT;
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-      vi[q] = rows[rec[slot][q].ij & 0xFFFFu];
-      vj[q] = rows[rec[slot][q].ij >> 16];
-    }
+    for (int q0 = 0; q0 < PPT; q0 += B) {
+      V vi[B], vj[B];
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-      if (EXACT || (TIGHT && q + 1 < PPT) || tid + q * NT < P) {
-        const float c = rec[slot][q].c, s = rec[slot][q].s;
-        rows[rec[slot][q].ij & 0xFFFFu] = c * vi[q] + s * vj[q];
-        rows[rec[slot][q].ij >> 16] = c * vj[q] - s * vi[q];
+      for (int b = 0; b < B; ++b) {
+        if (q0 + b < PPT) {
+          vi[b] = rows[rec[slot][q0 + b].ij & 0xFFFFu];
+          vj[b] = rows[rec[slot][q0 + b].ij >> 16];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int q = q0 + b;
+        if (q < PPT && (EXACT || (TIGHT && q + 1 < PPT) || tid + q * NT < P)) {
+          const float c = rec[slot][q].c, s = rec[slot][q].s;
+          rows[rec[slot][q].ij & 0xFFFFu] = c * vi[b] + s * vj[b];
+          rows[rec[slot][q].ij >> 16] = c * vj[b] - s * vi[b];
+        }
       }
     }
   }
