@@ -265,20 +265,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs p) {
   for (int i = 0; i < PD; ++i) load(reg[i], i);
   store(reg[0], 0, 0);
   __syncthreads();
-  for (int j = 0; j < ns; j += U) {
+  auto step = [&](int t, int u) {
+    load(reg[u % PD], t + PD);
+    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the stage's MFMAs
+    compute(u & 1, (u & 1) == 0);
+    if (t + 1 < ns) store(reg[(u + 1) % PD], (u + 1) & 1, t + 1);
+    __syncthreads();
+  };
+  // Whole iterations carry no branch around the loads, so the compiler's wait counts stay
+  // exact (a stage waits for its own loads only); the remainder (ns is even: 0, 2 or 4 steps)
+  // follows them.
+  const int nfull = ns - ns % U;
+  for (int j = 0; j < nfull; j += U) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = j + u;
-      if (u < 2 || t < ns) {  // ns is even: the first two steps always run
-        load(reg[u % PD], t + PD);
-        __builtin_amdgcn_sched_barrier(0);  // issue the loads before the stage's MFMAs
-        compute(u & 1, (u & 1) == 0);
-        if (u + 1 < U || t + 1 < ns) {
-          if (t + 1 < ns) store(reg[(u + 1) % PD], (u + 1) & 1, t + 1);
-        }
-        __syncthreads();
-      }
-    }
+    for (int u = 0; u < U; ++u) step(j + u, u);
+  }
+  if (nfull < ns) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (nfull + u < ns) step(nfull + u, u);
   }
 
   // ---- epilogue: multiply by the last group's scale and store (or store the split's partial)
@@ -419,16 +424,12 @@ hipError_t launch_block(int M, int D, int N, const uint16_t* x, bool x_nibble_or
     e = x_nibble_order ? launch_tile<bm, bn, wm, pd, true>(a, st) : launch_tile<bm, bn, wm, pd, false>(a, st);
   PARO_GEMM_CASE(128, 256, 1, 2)
   PARO_GEMM_CASE(128, 128, 1, 2)
-  PARO_GEMM_CASE(128, 128, 1, 3)
   PARO_GEMM_CASE(64, 256, 1, 2)
-  PARO_GEMM_CASE(64, 256, 1, 3)
   PARO_GEMM_CASE(128, 192, 2, 2)
   PARO_GEMM_CASE(128, 128, 2, 2)
-  PARO_GEMM_CASE(128, 128, 2, 3)
   PARO_GEMM_CASE(64, 256, 2, 2)
   PARO_GEMM_CASE(64, 192, 2, 2)
   PARO_GEMM_CASE(64, 128, 2, 2)
-  PARO_GEMM_CASE(64, 128, 2, 4)
 #undef PARO_GEMM_CASE
   if (e != hipSuccess || g.splits == 1) return e;
   const size_t count = size_t(M) * N;

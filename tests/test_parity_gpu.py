@@ -215,7 +215,10 @@ def test_linear_parity(wid, index, M):
 
 @pytest.mark.parametrize("M,D,N,K", [(1, 128, 1, 1), (2, 384, 200, 3), (3, 640, 77, 2), (4, 256, 513, 0),
                                      (5, 384, 200, 3), (17, 1280, 130, 4), (33, 512, 64, 2), (65, 768, 96, 8),
-                                     (130, 1024, 300, 5), (257, 384, 129, 1), (1, 16384, 40, 2), (6, 16384, 20, 2)])
+                                     (130, 1024, 300, 5), (257, 384, 129, 1), (1, 16384, 40, 2), (6, 16384, 20, 2),
+                                     # a few dozen rows: one group, ragged columns, deep reductions
+                                     (20, 128, 1, 2), (40, 1152, 513, 0), (48, 16384, 300, 1), (64, 4096, 257, 3),
+                                     (50, 2304, 1000, 8)])
 def test_linear_edge_shapes(M, D, N, K):
     L = W.custom_linear(21, M, D, N, K)
     C.log(f"linear edge M={M} D={D} N={N} K={K}")
@@ -235,6 +238,29 @@ def test_identity_transform_matches_plain_linear(M):
         a = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z, out_dtype=dt))
         b = C.host(rl.paro_w4a16_linear(xd, qw, sc, z, out_dtype=dt))
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_split_reduction_and_fallback():
+    """M = 64: with a workspace the reduction over D is split and the float32 partial sums are
+    added in split order; without one the call does not split. Both match the oracle, the
+    split call is deterministic, and the two differ only in float32 summation order."""
+    L = W.custom_linear(43, 64, 4096, 600, 2)
+    C.log("split / unsplit reduction M=64 D=4096 N=600")
+    op = O.pack_weights(L.W, L.pairs, L.theta, L.scale)
+    qw, sc, z = (C.dev(t, torch) for t in op)
+    xd = C.dev(L.x, torch)
+    need = rl.paro_workspace_bytes(64, 4096, 600)
+    ref = L.x.astype(np.float64) @ O.dequantize(*op).T
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    a = C.host(rl.paro_w4a16_linear(xd, qw, sc, z, out_dtype=torch.float32, ws=ws))
+    b = C.host(rl.paro_w4a16_linear(xd, qw, sc, z, out_dtype=torch.float32, ws=ws))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c = C.host(rl.paro_w4a16_linear(xd, qw, sc, z, out_dtype=torch.float32,
+                                    ws=torch.empty(256, dtype=torch.uint8, device="cuda")))
+    for y in (a, c):
+        mx, rel = C.linear_metrics(y, ref)
+        assert mx <= C.MAX_ABS and rel <= C.REL_L2, (mx, rel)
+    assert np.abs(a - c).max() <= 1e-4 * np.abs(ref).max()
 
 
 def test_empty_inputs_are_noops():
