@@ -128,8 +128,8 @@ __device__ inline void unit_fill(float* rot, float* isl, const uint32_t (&xp)[kF
         f0[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(xp[u][r])));
         f1[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(xp[u][r] >> 16)));
       }
-      rv[2 * cp] = *reinterpret_cast<const V*>(f0);
-      rv[2 * cp + 1] = *reinterpret_cast<const V*>(f1);
+      rv[2 * cp] = make_vec<R>(f0);
+      rv[2 * cp + 1] = make_vec<R>(f1);
     }
   }
 }
@@ -149,13 +149,11 @@ __device__ inline void unit_finish(StageRing<kThreads, PPT, PD, false, true>& ri
     const int c8 = j >> 2, e = j & 3, ca = 8 * c8 + e;
     const V va = rv[ca], vb = rv[ca + 4];
     const float sa = isl[ca], sb = isl[ca + 4];
-    const float* fa = reinterpret_cast<const float*>(&va);
-    const float* fb = reinterpret_cast<const float*>(&vb);
 #pragma unroll
     for (int m = 0; m < R; ++m)
       if (m < rows) {
-        const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fa[m] * sa));
-        const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fb[m] * sb));
+        const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(vec_at<R>(va, m) * sa));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(vec_at<R>(vb, m) * sb));
         xs32[(c8 * rows + m) * 4 + e] = lo | (hi << 16);
       }
   }

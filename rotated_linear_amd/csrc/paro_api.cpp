@@ -345,24 +345,44 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     if (!group.empty())
       if (hipError_t e = launch_decode(D, ydtype, group.data(), int(group.size()), st)) return from_hip(e);
   }
-  // the rest, one call at a time
+  // the rest: every call owns a consecutive slice of ws (for a rotated call: its transformed x,
+  // then its linear's partial sums). The transforms of one D run as one batched launch, then
+  // the linears one after the other.
+  std::vector<char*> slice(size_t(count > 0 ? count : 0), nullptr);
   char* wsp = static_cast<char*>(ws);
   for (int i = 0; i < count; ++i) {
     if (done[i]) continue;
     const paro_linear_args& c = calls[i];
-    const uint16_t* xh = static_cast<const uint16_t*>(c.x);
+    slice[i] = wsp;
+    wsp += c.rot ? rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) : linear_ws_bytes(c.M, c.D, c.N);
+  }
+  std::vector<char> rotated(size_t(count > 0 ? count : 0), 0);
+  for (int i = 0; i < count; ++i) {
+    if (done[i] || !calls[i].rot || rotated[i]) continue;
+    std::vector<RotateJob> jobs;
+    for (int j = i; j < count; ++j) {
+      const paro_linear_args& c = calls[j];
+      if (done[j] || !c.rot || rotated[j] || c.D != calls[i].D) continue;
+      rots[j] = dev_rot(*c.rot);
+      jobs.push_back(RotateJob{&rots[j], c.M, static_cast<const uint16_t*>(c.x), reinterpret_cast<uint16_t*>(slice[j])});
+      rotated[j] = 1;
+    }
+    if (hipError_t e = launch_rotate_batch(jobs.data(), int(jobs.size()), true, st)) return from_hip(e);
+  }
+  for (int i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    const paro_linear_args& c = calls[i];
     const uint16_t* sc = static_cast<const uint16_t*>(c.scales);
     const uint16_t* zr = static_cast<const uint16_t*>(c.zeros);
     paro_status s;
     if (c.rot) {
-      const DevRot R = dev_rot(*c.rot);
-      const size_t part = rotated_ws_bytes(R.K, c.M, c.D, c.N);
-      s = run_rotated_two_step(R, c.M, c.N, xh, c.qweight, sc, zr, c.y, ydtype, wsp, part, st);
-      wsp += part;
+      const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
+      const size_t part = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+      s = run_linear(c.M, c.D, c.N, reinterpret_cast<const uint16_t*>(slice[i]), true, c.qweight, sc, zr, c.y,
+                     ydtype, slice[i] + xr_bytes, part, st);
     } else {
-      const size_t part = linear_ws_bytes(c.M, c.D, c.N);
-      s = run_linear(c.M, c.D, c.N, xh, false, c.qweight, sc, zr, c.y, ydtype, wsp, part, st);
-      wsp += part;
+      s = run_linear(c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight, sc, zr, c.y, ydtype,
+                     slice[i], linear_ws_bytes(c.M, c.D, c.N), st);
     }
     if (s != PARO_OK) return s;
   }

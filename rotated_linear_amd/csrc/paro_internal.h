@@ -119,6 +119,16 @@ hipError_t launch_pack(const DevRot& R, int N, const uint16_t* W, uint8_t* qweig
 // nibble_order: write each 8-channel word as [0,4,1,5,2,6,3,7] (the decode kernel's A order).
 hipError_t launch_rotate(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, bool nibble_order,
                          hipStream_t st);
+// Several transforms of the same D (each with its own descriptor, x and output) in as few
+// launches as the GPU holds at once (up to kRotMaxJobs per launch).
+constexpr int kRotMaxJobs = 16;
+struct RotateJob {
+  const DevRot* R;
+  int M;
+  const uint16_t* x;
+  uint16_t* xout;
+};
+hipError_t launch_rotate_batch(const RotateJob* jobs, int n, bool nibble_order, hipStream_t st);
 // Tiling of the prefill GEMM (gemm.hip): a BM x BN output tile per workgroup, the reduction
 // over D split into `splits` ranges of groups whose float32 partial sums a second kernel adds.
 struct GemmPlan {

@@ -23,6 +23,8 @@
 // With PERM the output keeps every 8-channel word in the order the INT4 decode of
 // the linear kernels produces ([0,4,1,5,2,6,3,7]), which is how
 // paro_rotated_linear hands its workspace to them.
+#include <string.h>
+
 #include <algorithm>
 
 #include "rotation_core.h"
@@ -42,15 +44,34 @@ __device__ inline int fresh_tid() {
   return t;
 }
 
+// A launch serves one or more jobs (calls) of the same D: workgroup b belongs to the job whose
+// block range [blk0[j], blk0[j+1]) holds b and never changes jobs: a single job is walked by
+// persistent workgroups (stride gridDim.x); with several jobs the grid is their total block
+// count, one block per workgroup.
+struct RotJobs {
+  const uint16_t* x[kRotMaxJobs];
+  uint16_t* xout[kRotMaxJobs];
+  const PairRec* rec[kRotMaxJobs];
+  const float* inv_s[kRotMaxJobs];
+  int M[kRotMaxJobs];
+  int K[kRotMaxJobs];
+  int blk0[kRotMaxJobs + 1];
+  int n, D;
+};
+
 template <int NT, int R, int PPT, int PD, bool EXACT, bool PERM>
-__global__ __launch_bounds__(NT) void rotate_rows_kernel(const uint16_t* __restrict__ x,
-                                                                   uint16_t* __restrict__ xout, int M, int D,
-                                                                   int K, const PairRec* recs,
-                                                                   const float* __restrict__ inv_s) {
+__global__ __launch_bounds__(NT) void rotate_rows_kernel(const RotJobs J) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [D][R]
   const int tid = threadIdx.x;
+  int job = 0;
+  while (job + 1 < J.n && int(blockIdx.x) >= J.blk0[job + 1]) ++job;  // uniform
+  const uint16_t* const x = J.x[job];
+  uint16_t* const xout = J.xout[job];
+  const PairRec* const recs = J.rec[job];
+  const float* const inv_s = J.inv_s[job];
+  const int M = J.M[job], K = J.K[job], D = J.D;
   const int P = D / 2;
-  const int nblk = (M + R - 1) / R;  // the grid never exceeds it
+  const int nblk = (M + R - 1) / R;
   using V = typename RowVec<R>::T;
   V* rows = reinterpret_cast<V*>(lds);
 
@@ -105,8 +126,8 @@ __global__ __launch_bounds__(NT) void rotate_rows_kernel(const uint16_t* __restr
           f0[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r])));
           f1[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r] >> 16)));
         }
-        rows[2 * cp] = *reinterpret_cast<const V*>(f0);
-        rows[2 * cp + 1] = *reinterpret_cast<const V*>(f1);
+        rows[2 * cp] = make_vec<R>(f0);
+        rows[2 * cp + 1] = make_vec<R>(f1);
       }
     }
   };
@@ -114,7 +135,7 @@ __global__ __launch_bounds__(NT) void rotate_rows_kernel(const uint16_t* __restr
   // Software pipeline over the workgroup's blocks of R rows: the next block's rows are loaded
   // while this block's stages run, and this block's output leaves from registers while the
   // next block's stages run, so global traffic overlaps the LDS-bound stages.
-  int blk = blockIdx.x;
+  int blk = int(blockIdx.x) - J.blk0[job];  // < nblk: the grid never exceeds a job's blocks
   load_rows(blk);
   StageRing<NT, PPT, PD, EXACT> ring;
   if (K > 0) ring_prime(ring, K, P, tid, recs);
@@ -135,12 +156,10 @@ __global__ __launch_bounds__(NT) void rotate_rows_kernel(const uint16_t* __restr
       const int j = min(to + u * NT, P - 1);
       const int ca = PERM ? 8 * (j >> 2) + (j & 3) : 2 * j, cb = PERM ? ca + 4 : ca + 1;
       const V va = rows[ca], vb = rows[cb];
-      const float* fa = reinterpret_cast<const float*>(&va);
-      const float* fb = reinterpret_cast<const float*>(&vb);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fa[r] * isa[u]));
-        const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fb[r] * isc[u]));
+        const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(vec_at<R>(va, r) * isa[u]));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(vec_at<R>(vb, r) * isc[u]));
         ov[u][r] = lo | (hi << 16);
       }
     }
@@ -169,55 +188,78 @@ __global__ __launch_bounds__(NT) void rotate_rows_kernel(const uint16_t* __restr
   }
 }
 
+// One launch over J (jobs of one D), `grid` workgroups.
 template <int NT, int R, int PPT, int PD, bool EXACT, bool PERM>
-hipError_t launch_rows(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  const size_t lds = size_t(Rt.D) * R * sizeof(float);
+hipError_t launch_rows(const RotJobs& J, int grid, hipStream_t st) {
+  const size_t lds = size_t(J.D) * R * sizeof(float);
   const void* fn = reinterpret_cast<const void*>(&rotate_rows_kernel<NT, R, PPT, PD, EXACT, PERM>);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  const long nblk = (M + R - 1) / R;
-  const long per_cu = std::max<long>(1, long(kRotLds / lds));  // workgroups one CU holds at once
-  const int grid = int(std::min<long>(nblk, per_cu * kCUs));
-  hipLaunchKernelGGL((rotate_rows_kernel<NT, R, PPT, PD, EXACT, PERM>), dim3(grid), dim3(NT), lds, st, x, xout, M,
-                     Rt.D, Rt.K, Rt.rec, Rt.inv_s);
+  hipLaunchKernelGGL((rotate_rows_kernel<NT, R, PPT, PD, EXACT, PERM>), dim3(grid), dim3(NT), lds, st, J);
   return hipGetLastError();
 }
 
 template <int NT, int R, int PPT, int PD, bool PERM>
-hipError_t launch_exact(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  if (Rt.D / 2 == PPT * NT) return launch_rows<NT, R, PPT, PD, true, PERM>(Rt, M, x, xout, st);
-  return launch_rows<NT, R, PPT, PD, false, PERM>(Rt, M, x, xout, st);
+hipError_t launch_exact(const RotJobs& J, int grid, hipStream_t st) {
+  if (J.D / 2 == PPT * NT) return launch_rows<NT, R, PPT, PD, true, PERM>(J, grid, st);
+  return launch_rows<NT, R, PPT, PD, false, PERM>(J, grid, st);
 }
 
 // Threads, pairs per thread per stage (PPT) and ring depth by row width (the ring is shallower
 // for wide rows, whose records and row vectors take more registers).
 template <int R, bool PERM>
-hipError_t launch_ppt(const DevRot& Rt, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  const int P = Rt.D / 2;
-  if (P <= 512) return launch_exact<512, R, 1, 8, PERM>(Rt, M, x, xout, st);
-  if (P <= 1024) return launch_exact<512, R, 2, 8, PERM>(Rt, M, x, xout, st);
-  if (P <= 1536) return launch_exact<512, R, 3, 4, PERM>(Rt, M, x, xout, st);
-  if (P <= 2048) return launch_exact<512, R, 4, 4, PERM>(Rt, M, x, xout, st);
-  if (P <= 3072) return launch_exact<512, R, 6, 2, PERM>(Rt, M, x, xout, st);
-  if (P <= 4608) return launch_exact<512, R, 9, 2, PERM>(Rt, M, x, xout, st);
+hipError_t launch_ppt(const RotJobs& J, int grid, hipStream_t st) {
+  const int P = J.D / 2;
+  if (P <= 512) return launch_exact<512, R, 1, 8, PERM>(J, grid, st);
+  if (P <= 1024) return launch_exact<512, R, 2, 8, PERM>(J, grid, st);
+  if (P <= 1536) return launch_exact<512, R, 3, 4, PERM>(J, grid, st);
+  if (P <= 2048) return launch_exact<512, R, 4, 4, PERM>(J, grid, st);
+  if (P <= 3072) return launch_exact<512, R, 6, 2, PERM>(J, grid, st);
+  if (P <= 4608) return launch_exact<512, R, 9, 2, PERM>(J, grid, st);
   if constexpr (R <= 2) {  // wider rows (D > 9216) never take 4 rows per workgroup
-    if (P <= 6144) return launch_exact<512, R, 12, 2, PERM>(Rt, M, x, xout, st);
-    if (P <= 7168) return launch_exact<512, R, 14, 1, PERM>(Rt, M, x, xout, st);
-    return launch_exact<512, R, 16, 1, PERM>(Rt, M, x, xout, st);
+    if (P <= 6144) return launch_exact<512, R, 12, 2, PERM>(J, grid, st);
+    if (P <= 7168) return launch_exact<512, R, 14, 1, PERM>(J, grid, st);
+    return launch_exact<512, R, 16, 1, PERM>(J, grid, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <bool PERM>
-hipError_t launch_r(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, hipStream_t st) {
-  // Rows per workgroup: a stage's parameters are read once per block, so larger blocks
-  // save their traffic once there are enough rows to give every CU a block.
-  const size_t row_bytes = size_t(R.D) * 4;
-  if (M >= 4 * kCUs && 4 * row_bytes <= kRotLds && R.D <= 9216) return launch_ppt<4, PERM>(R, M, x, xout, st);
-  if (M >= 2 * kCUs && 2 * row_bytes <= kRotLds) return launch_ppt<2, PERM>(R, M, x, xout, st);
-  return launch_ppt<1, PERM>(R, M, x, xout, st);
+// Rows per workgroup: a stage's parameters are read once per block, so larger blocks save
+// their traffic once there are enough rows (the smallest job's) to give every CU a block.
+int rows_per_block(int D, int M) {
+  const size_t row_bytes = size_t(D) * 4;
+  if (M >= 4 * kCUs && 4 * row_bytes <= kRotLds && D <= 9216) return 4;
+  if (M >= 2 * kCUs && 2 * row_bytes <= kRotLds) return 2;
+  return 1;
+}
+
+// Launch jobs[0, n) (same D, 1 <= n <= kRotMaxJobs) with R rows per block: one job on
+// persistent workgroups, several jobs one block per workgroup (the caller keeps their total
+// within what the GPU holds at once).
+hipError_t launch_jobs(const RotateJob* jobs, int n, int R, bool perm, hipStream_t st) {
+  RotJobs J;
+  memset(&J, 0, sizeof(J));
+  J.n = n;
+  J.D = jobs[0].R->D;
+  int total = 0;
+  for (int i = 0; i < n; ++i) {
+    J.x[i] = jobs[i].x;
+    J.xout[i] = jobs[i].xout;
+    J.rec[i] = jobs[i].R->rec;
+    J.inv_s[i] = jobs[i].R->inv_s;
+    J.M[i] = jobs[i].M;
+    J.K[i] = jobs[i].R->K;
+    J.blk0[i] = total;
+    total += (jobs[i].M + R - 1) / R;
+  }
+  J.blk0[n] = total;
+  const long per_cu = std::max<long>(1, long(kRotLds / (size_t(J.D) * R * sizeof(float))));
+  const int grid = n == 1 ? int(std::min<long>(total, per_cu * kCUs)) : total;
+  if (R == 4) return perm ? launch_ppt<4, true>(J, grid, st) : launch_ppt<4, false>(J, grid, st);
+  if (R == 2) return perm ? launch_ppt<2, true>(J, grid, st) : launch_ppt<2, false>(J, grid, st);
+  return perm ? launch_ppt<1, true>(J, grid, st) : launch_ppt<1, false>(J, grid, st);
 }
 
 }  // namespace
@@ -225,7 +267,39 @@ hipError_t launch_r(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, h
 hipError_t launch_rotate(const DevRot& R, int M, const uint16_t* x, uint16_t* xout, bool nibble_order,
                          hipStream_t st) {
   if (R.D / 2 > 8 * 1024) return hipErrorInvalidValue;
-  return nibble_order ? launch_r<true>(R, M, x, xout, st) : launch_r<false>(R, M, x, xout, st);
+  const RotateJob job{&R, M, x, xout};
+  return launch_jobs(&job, 1, rows_per_block(R.D, M), nibble_order, st);
+}
+
+hipError_t launch_rotate_batch(const RotateJob* jobs, int n, bool nibble_order, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int D = jobs[0].R->D;
+  int min_m = jobs[0].M;
+  for (int i = 0; i < n; ++i) {
+    if (jobs[i].R->D != D || jobs[i].M <= 0) return hipErrorInvalidValue;
+    min_m = std::min(min_m, jobs[i].M);
+  }
+  if (D / 2 > 8 * 1024) return hipErrorInvalidValue;
+  if (n == 1) return launch_rotate(*jobs[0].R, jobs[0].M, jobs[0].x, jobs[0].xout, nibble_order, st);
+  // several jobs: one block per workgroup, each launch within what the GPU holds at once
+  const int R = rows_per_block(D, min_m);
+  const long cap = std::max<long>(1, long(kRotLds / (size_t(D) * R * sizeof(float)))) * kCUs;
+  int i0 = 0;
+  while (i0 < n) {
+    long blocks = 0;
+    int i1 = i0;
+    while (i1 < n && i1 - i0 < kRotMaxJobs) {
+      const long b = (jobs[i1].M + R - 1) / R;
+      if (i1 > i0 && blocks + b > cap) break;
+      blocks += b;
+      ++i1;
+    }
+    hipError_t e = blocks > cap ? launch_rotate(*jobs[i0].R, jobs[i0].M, jobs[i0].x, jobs[i0].xout, nibble_order, st)
+                                : launch_jobs(jobs + i0, i1 - i0, R, nibble_order, st);
+    if (e != hipSuccess) return e;
+    i0 = i1;
+  }
+  return hipSuccess;
 }
 
 }  // namespace paro

@@ -34,6 +34,28 @@ struct RowVec<1> {
   using T = float;
 };
 
+// Build an R-row channel vector from its rows / read row r of one, without taking the address
+// of a local array (which can send it to scratch memory).
+template <int R>
+__device__ inline typename RowVec<R>::T make_vec(const float (&f)[R]) {
+  if constexpr (R == 1) {
+    return f[0];
+  } else if constexpr (R == 2) {
+    return typename RowVec<R>::T{f[0], f[1]};
+  } else {
+    static_assert(R == 4, "rows per vector: 1, 2 or 4");
+    return typename RowVec<R>::T{f[0], f[1], f[2], f[3]};
+  }
+}
+template <int R>
+__device__ inline float vec_at(const typename RowVec<R>::T& v, int r) {
+  if constexpr (R == 1) {
+    return v;
+  } else {
+    return v[r];
+  }
+}
+
 template <int NT, int PPT, int PD, bool EXACT, bool TIGHT = false>
 struct StageRing {
   PairRec rec[PD][PPT];
