@@ -8,6 +8,7 @@
 // to execute"). Thread t owns pairs t, t + NT, ... of every stage; the host
 // orders each stage so a wave's gathers spread over the LDS banks.
 //
+// Per row: x_i <- fma(c, x_i, s x_j), x_j <- fma(c, x_j, -(s x_i)) in float32.
 // Each pair is one 12-byte record {i | j << 16, cos, sin}: one 3-dword load.
 // The records of PD stages are kept in flight in a register ring: loading
 // stage k + PD is issued right after stage k. Loads are branch-free (indices
@@ -53,6 +54,19 @@ __device__ inline float vec_at(const typename RowVec<R>::T& v, int r) {
     return v;
   } else {
     return v[r];
+  }
+}
+
+// One output of the 2x2 rotation, c * a + t with t = +-(s * b) already rounded: written as an
+// explicit fused multiply-add so every kernel and every R (scalar or vector code) rounds the
+// same way, and a row's result does not depend on how many rows share its workgroup.
+template <int R>
+__device__ inline typename RowVec<R>::T givens_fma(float c, typename RowVec<R>::T a, typename RowVec<R>::T t) {
+  if constexpr (R == 1) {
+    return __builtin_fmaf(c, a, t);
+  } else {
+    using V = typename RowVec<R>::T;
+    return __builtin_elementwise_fma(V{} + c, a, t);
   }
 }
 
@@ -112,8 +126,8 @@ struct StageRing {
         const int q = q0 + b;
         if (q < PPT && (EXACT || (TIGHT && q + 1 < PPT) || tid + q * NT < P)) {
           const float c = rec[slot][q].c, s = rec[slot][q].s;
-          rows[rec[slot][q].ij & 0xFFFFu] = c * vi[b] + s * vj[b];
-          rows[rec[slot][q].ij >> 16] = c * vj[b] - s * vi[b];
+          rows[rec[slot][q].ij & 0xFFFFu] = givens_fma<R>(c, vi[b], s * vj[b]);
+          rows[rec[slot][q].ij >> 16] = givens_fma<R>(c, vj[b], -(s * vi[b]));
         }
       }
     }

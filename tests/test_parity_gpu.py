@@ -323,6 +323,10 @@ def _single(rot, xd, w, dt):
     # plain and rotated mixed, ragged N, several D, a prefill-sized call and a deep transform
     [(70, 3, 768, 200, 8), (71, 16, 768, 77, None), (72, 5, 2048, 130, 2), (73, 1, 2048, 16, None),
      (74, 40, 768, 96, 8), (75, 2, 768, 64, 12), (76, 7, 8960 // 70 * 70, 33, 8), (77, 1, 4096, 300, 8)],
+    # 20 transforms of one D with M > 16 (two batched transform launches of up to 16 jobs),
+    # ragged M, K from 0 to 12, plus plain calls in between
+    [(90 + i, 17 + 3 * i, 512, 40 + i, [2, 8, 12, 0][i % 4]) for i in range(20)]
+    + [(120, 33, 512, 64, None), (121, 300, 512, 96, None)],
 ])
 def test_batch_matches_single_calls_bitwise(specs):
     C.log(f"batch of {len(specs)} calls")
