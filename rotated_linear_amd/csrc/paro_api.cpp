@@ -266,6 +266,9 @@ paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void
 
 // ---- batches -------------------------------------------------------------------------------
 
+// Calls up to this many rows have their transforms batched into shared launches.
+constexpr int kBatchTransformMaxM = 256;
+
 static size_t batch_ws_bytes(int count, const paro_linear_args* calls) {
   size_t total = 0;
   for (int i = 0; i < count; ++i)
@@ -346,8 +349,9 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
       if (hipError_t e = launch_decode(D, ydtype, group.data(), int(group.size()), st)) return from_hip(e);
   }
   // the rest: every call owns a consecutive slice of ws (for a rotated call: its transformed x,
-  // then its linear's partial sums). The transforms of one D run as one batched launch, then
-  // the linears one after the other.
+  // then its linear's partial sums). The transforms of the short calls (M <= 256) that share D
+  // run as one batched launch, then the linears one after the other; a long call's transform
+  // runs right before its linear, whose x' is then still in the caches.
   std::vector<char*> slice(size_t(count > 0 ? count : 0), nullptr);
   char* wsp = static_cast<char*>(ws);
   for (int i = 0; i < count; ++i) {
@@ -358,11 +362,11 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
   }
   std::vector<char> rotated(size_t(count > 0 ? count : 0), 0);
   for (int i = 0; i < count; ++i) {
-    if (done[i] || !calls[i].rot || rotated[i]) continue;
+    if (done[i] || !calls[i].rot || rotated[i] || calls[i].M > kBatchTransformMaxM) continue;
     std::vector<RotateJob> jobs;
     for (int j = i; j < count; ++j) {
       const paro_linear_args& c = calls[j];
-      if (done[j] || !c.rot || rotated[j] || c.D != calls[i].D) continue;
+      if (done[j] || !c.rot || rotated[j] || c.D != calls[i].D || c.M > kBatchTransformMaxM) continue;
       rots[j] = dev_rot(*c.rot);
       jobs.push_back(RotateJob{&rots[j], c.M, static_cast<const uint16_t*>(c.x), reinterpret_cast<uint16_t*>(slice[j])});
       rotated[j] = 1;
@@ -378,6 +382,12 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     if (c.rot) {
       const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
       const size_t part = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+      if (!rotated[i]) {
+        rots[i] = dev_rot(*c.rot);
+        if (hipError_t e = launch_rotate(rots[i], c.M, static_cast<const uint16_t*>(c.x),
+                                         reinterpret_cast<uint16_t*>(slice[i]), true, st))
+          return from_hip(e);
+      }
       s = run_linear(c.M, c.D, c.N, reinterpret_cast<const uint16_t*>(slice[i]), true, c.qweight, sc, zr, c.y,
                      ydtype, slice[i] + xr_bytes, part, st);
     } else {

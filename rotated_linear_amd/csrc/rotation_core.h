@@ -72,7 +72,9 @@ __device__ inline typename RowVec<R>::T givens_fma(float c, typename RowVec<R>::
 
 template <int NT, int PPT, int PD, bool EXACT, bool TIGHT = false>
 struct StageRing {
-  PairRec rec[PD][PPT];
+  // a slot's records as three plain arrays (an array of structs can end up in scratch memory)
+  uint32_t ij[PD][PPT];
+  float cs[PD][PPT], sn[PD][PPT];
 
   // Issue the loads of stage k (clamped into [0, K)) into ring slot `slot`: a uniform stage
   // base plus a 32-bit per-lane byte offset (the same offsets serve every stage, so no
@@ -94,9 +96,9 @@ struct StageRing {
       // three 4-byte-aligned words (a 12-byte record; one dwordx3 load)
       typedef __attribute__((address_space(1))) const uint32_t* gwords;
       const gwords w = reinterpret_cast<gwords>(sb + uint32_t(p) * uint32_t(sizeof(PairRec)));
-      rec[slot][q].ij = w[0];
-      rec[slot][q].c = __builtin_bit_cast(float, w[1]);
-      rec[slot][q].s = __builtin_bit_cast(float, w[2]);
+      ij[slot][q] = w[0];
+      cs[slot][q] = __builtin_bit_cast(float, w[1]);
+      sn[slot][q] = __builtin_bit_cast(float, w[2]);
     }
   }
 
@@ -117,17 +119,17 @@ struct StageRing {
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         if (q0 + b < PPT) {
-          vi[b] = rows[rec[slot][q0 + b].ij & 0xFFFFu];
-          vj[b] = rows[rec[slot][q0 + b].ij >> 16];
+          vi[b] = rows[ij[slot][q0 + b] & 0xFFFFu];
+          vj[b] = rows[ij[slot][q0 + b] >> 16];
         }
       }
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const int q = q0 + b;
         if (q < PPT && (EXACT || (TIGHT && q + 1 < PPT) || tid + q * NT < P)) {
-          const float c = rec[slot][q].c, s = rec[slot][q].s;
-          rows[rec[slot][q].ij & 0xFFFFu] = givens_fma<R>(c, vi[b], s * vj[b]);
-          rows[rec[slot][q].ij >> 16] = givens_fma<R>(c, vj[b], -(s * vi[b]));
+          const float c = cs[slot][q], s = sn[slot][q];
+          rows[ij[slot][q] & 0xFFFFu] = givens_fma<R>(c, vi[b], s * vj[b]);
+          rows[ij[slot][q] >> 16] = givens_fma<R>(c, vj[b], -(s * vi[b]));
         }
       }
     }

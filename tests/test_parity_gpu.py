@@ -326,7 +326,7 @@ def _single(rot, xd, w, dt):
     # 20 transforms of one D with M > 16 (two batched transform launches of up to 16 jobs),
     # ragged M, K from 0 to 12, plus plain calls in between
     [(90 + i, 17 + 3 * i, 512, 40 + i, [2, 8, 12, 0][i % 4]) for i in range(20)]
-    + [(120, 33, 512, 64, None), (121, 300, 512, 96, None)],
+    + [(120, 33, 512, 64, None), (121, 300, 512, 96, None), (122, 300, 512, 96, 8)],
 ])
 def test_batch_matches_single_calls_bitwise(specs):
     C.log(f"batch of {len(specs)} calls")
