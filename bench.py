@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--traffic", action="store_true",
                    help="for rocprofv3 --pmc runs: a 256 MiB float16 negation (the counter calibration copy) "
                         "and then the dominant call over the cold pool, eagerly; prints nothing else")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="for rocprofv3 runs: only the down_proj prefill (M=2048, D=8960, N=1536), --steps rotated "
+                        "then --steps plain calls, eagerly; prints one line of event timings")
     return p.parse_args()
 
 
@@ -238,6 +241,9 @@ def main():
     if args.traffic:
         traffic_run(rl, torch, W, args.steps)
         return
+    if args.prefill_only:
+        prefill_run(rl, torch, W, args.steps)
+        return
     step, pool_bytes = attention_step(rl, torch, W)
     n_slots = step.n_slots
     per_graph = math.gcd(args.steps, 8) or 1  # steps per captured graph (divides K exactly)
@@ -348,6 +354,26 @@ def traffic_run(rl, torch, W, reps):
         st.enqueue(r, rotated=True, batched=True)
     torch.cuda.synchronize()
     print(json.dumps({"traffic_run": {"steps": reps, "calib_bytes": CALIB_BYTES}}), flush=True)
+
+
+def prefill_run(rl, torch, W, reps):
+    """The down_proj prefill alone (rotated, then plain), for kernel traces and counters."""
+    L4 = Linear(rl, torch, W.make_linear(4, 0))
+    st = Step(rl, torch, [L4], [2048])
+    out = {}
+    for rotated in (True, False):
+        for _ in range(3):
+            st.enqueue(0, rotated=rotated)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            st.enqueue(0, rotated=rotated)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out["rotated" if rotated else "plain"] = {"us": round(us, 2), "TFLOP/s": round(st.flops() / us / 1e6, 2)}
+    print(json.dumps({"prefill_only": "down_proj M=2048 D=8960 N=1536 K=8", **out}), flush=True)
 
 
 def extras(rl, torch, W, args):
