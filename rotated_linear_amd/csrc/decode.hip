@@ -128,8 +128,12 @@ __device__ inline void unit_fill(float* rot, float* isl, const uint32_t (&xp)[kF
         f0[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(xp[u][r])));
         f1[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(xp[u][r] >> 16)));
       }
-      rv[2 * cp] = make_vec<R>(f0);
-      rv[2 * cp + 1] = make_vec<R>(f1);
+      // lanes with bit 32/R set write their odd channel first: every aligned run of 16 (R = 4),
+      // 32 or 64 lanes then hits distinct bank slots in each of the two writes
+      const bool sw = (tid & (32 / R)) != 0;
+      const V v0 = make_vec<R>(f0), v1 = make_vec<R>(f1);
+      rv[2 * cp + (sw ? 1 : 0)] = sw ? v1 : v0;
+      rv[2 * cp + (sw ? 0 : 1)] = sw ? v0 : v1;
     }
   }
 }
@@ -147,7 +151,10 @@ __device__ inline void unit_finish(StageRing<kThreads, PPT, PD, false, true>& ri
   uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
   for (int j = tid; j < P; j += kThreads) {
     const int c8 = j >> 2, e = j & 3, ca = 8 * c8 + e;
-    const V va = rv[ca], vb = rv[ca + 4];
+    // read in the order that keeps each run of 32/R lanes on distinct bank slots (see unit_fill)
+    const bool sw = (tid & (32 / R)) != 0;
+    const V w1 = rv[sw ? ca + 4 : ca], w2 = rv[sw ? ca : ca + 4];
+    const V va = sw ? w2 : w1, vb = sw ? w1 : w2;
     const float sa = isl[ca], sb = isl[ca + 4];
 #pragma unroll
     for (int m = 0; m < R; ++m)

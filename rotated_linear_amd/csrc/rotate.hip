@@ -18,7 +18,8 @@
 // order gives exactly that for the R = 4 (2, 1) vectors (runs of 64, 32, 16 and 8
 // pairs with distinct residues modulo their length). Rows move between global
 // memory and LDS two adjacent channels per lane, so a wave's vector accesses
-// cover consecutive channels.
+// cover consecutive channels; lanes with bit 32/R set swap the order of their
+// two accesses, which keeps those passes on distinct bank slots too.
 //
 // With PERM the output keeps every 8-channel word in the order the INT4 decode of
 // the linear kernels produces ([0,4,1,5,2,6,3,7]), which is how
@@ -126,8 +127,12 @@ __global__ __launch_bounds__(NT) void rotate_rows_kernel(const RotJobs J) {
           f0[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r])));
           f1[r] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(hv[u][r] >> 16)));
         }
-        rows[2 * cp] = make_vec<R>(f0);
-        rows[2 * cp + 1] = make_vec<R>(f1);
+        // lanes with bit 32/R set write their odd channel first: every aligned run of 16 (R = 4),
+        // 32 or 64 lanes then hits distinct bank slots in each of the two writes
+        const bool sw = (tl & (32 / R)) != 0;
+        const V v0 = make_vec<R>(f0), v1 = make_vec<R>(f1);
+        rows[2 * cp + (sw ? 1 : 0)] = sw ? v1 : v0;
+        rows[2 * cp + (sw ? 0 : 1)] = sw ? v0 : v1;
       }
     }
   };
@@ -155,7 +160,10 @@ __global__ __launch_bounds__(NT) void rotate_rows_kernel(const RotJobs J) {
     for (int u = 0; u < PPT; ++u) {
       const int j = min(to + u * NT, P - 1);
       const int ca = PERM ? 8 * (j >> 2) + (j & 3) : 2 * j, cb = PERM ? ca + 4 : ca + 1;
-      const V va = rows[ca], vb = rows[cb];
+      // read in the order that keeps each run of 32/R lanes on distinct bank slots (see fill)
+      const bool sw = (to & (32 / R)) != 0;
+      const V w1 = rows[sw ? cb : ca], w2 = rows[sw ? ca : cb];
+      const V va = sw ? w2 : w1, vb = sw ? w1 : w2;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(vec_at<R>(va, r) * isa[u]));
