@@ -141,7 +141,11 @@ def test_rotate_identity_and_order():
 
 
 @pytest.mark.parametrize("M,D,K", [(1, 128, 0), (3, 128, 1), (5, 384, 3), (7, 16384, 2), (9, 1280, 8),
-                                   (130, 640, 5)])
+                                   (130, 640, 5),
+                                   # the most stages (rolled stage loop), one past the unrolled count
+                                   (20, 1024, 64), (6, 2048, 9),
+                                   # rows per block 2 and 4, widths at and past the 4-row limit
+                                   (300, 1536, 8), (600, 9216, 3), (1100, 9216, 2), (520, 9344, 2)])
 def test_rotate_edge_shapes(M, D, K):
     L = W.custom_linear(11, M, D, 4, K)
     C.log(f"rotate edge M={M} D={D} K={K}")
@@ -218,7 +222,9 @@ def test_linear_parity(wid, index, M):
                                      (130, 1024, 300, 5), (257, 384, 129, 1), (1, 16384, 40, 2), (6, 16384, 20, 2),
                                      # a few dozen rows: one group, ragged columns, deep reductions
                                      (20, 128, 1, 2), (40, 1152, 513, 0), (48, 16384, 300, 1), (64, 4096, 257, 3),
-                                     (50, 2304, 1000, 8)])
+                                     (50, 2304, 1000, 8),
+                                     # deep transforms on the two-kernel path
+                                     (3, 512, 100, 64), (40, 1024, 200, 33)])
 def test_linear_edge_shapes(M, D, N, K):
     L = W.custom_linear(21, M, D, N, K)
     C.log(f"linear edge M={M} D={D} N={N} K={K}")
