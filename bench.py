@@ -476,6 +476,124 @@ def extras(rl, torch, W, args):
                                  "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
     del st, L4
     res.update(layer8b(rl, torch, W, args))
+    res.update(overhead_vs_k(rl, torch, W, args))
+    res.update(model_stack(rl, torch, W, args))
+    return res
+
+
+def _with_stages(L, K):
+    """The same linear with only the first K of its transform's stages."""
+    import dataclasses
+    return dataclasses.replace(L, spec=dataclasses.replace(L.spec, K=K), pairs=L.pairs[:K], theta=L.theta[:K])
+
+
+def overhead_vs_k(rl, torch, W, args):
+    """Rotation overhead against the stage count (K = 0, 2, 4, 8) at the gate+up decode shape (M = 1,
+    cold pool) and the down_proj prefill shape (M = 2048), next to the dense alternative the pairwise
+    stages replace: a D x D float16 rotation applied to x by the vendor GEMM (torch.matmul), then the
+    plain INT4 linear."""
+    res = {}
+    for name, wid, M, per in (("gate_up_decode_M1", 3, 1, 8), ("down_prefill_M2048", 4, 2048, 4)):
+        base = W.make_linear(wid, 0)
+        entry = {}
+        for K in (0, 2, 4, 8):
+            lin = Linear(rl, torch, _with_stages(base, K))
+            n = max(4, math.ceil(POOL_BYTES / lin.set_bytes())) if M == 1 else 4
+            if M == 1:
+                lin.make_copies(rl, n)
+            st = Step(rl, torch, [lin], [M])
+            if K == 0:
+                ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), n, per, 2 * n, per)
+                entry["plain_us"] = round(ms_p * 1e3, 2)
+            ms_r = time_slots(torch, lambda s: st.enqueue(s), n, per, 2 * n, per)
+            entry[f"K{K}"] = {"us": round(ms_r * 1e3, 2), "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
+            if K == 8:  # the dense contrast, on the same packed weights and pool
+                D = lin.D
+                g = torch.Generator(device="cuda").manual_seed(K)
+                R = [torch.randn(D, D, device="cuda", generator=g).half() for _ in range(n if M == 1 else 1)]
+                x = st.x[(0, M)]
+                xr = torch.empty_like(x)
+
+                def dense(s):
+                    torch.matmul(x, R[s % len(R)], out=xr)
+                    rot, w = st._weights(0, M, s)
+                    rl.paro_w4a16_linear(xr, *w, out=st.y[(0, M)], ws=st.ws[(0, M)])
+                ms_d = time_slots(torch, dense, n, per, 2 * n, per)
+                entry["dense_fp16_rotation"] = {"us": round(ms_d * 1e3, 2),
+                                                "overhead_pct": round((ms_d - ms_p) / ms_p * 100, 2),
+                                                "rotation_bytes": D * D * 2, "rotation_flop": 2.0 * M * D * D}
+                del R
+            del st, lin
+        res[f"overhead_vs_K_{name}"] = entry
+    return res
+
+
+def model_stack(rl, torch, W, args):
+    """The 1.5B-shaped decoder stack (28 layers x q, k, v, o, gate, up, down; every linear with its
+    own transform): build throughput (folding, quantizing and packing all 196 weight matrices) and
+    the decode step at M = 1 over the whole stack, as one batched call (grouped launches) and as the
+    4 dependent launches per layer a decode step makes (q/k/v, o, gate/up, down). The packed stack
+    (about 0.8 GB) is three times the Infinity Cache, so each step reads it cold."""
+    res = {}
+    nl, specs = W.MODEL_LAYERS, W.MODEL_LINEARS
+    Ws = [torch.from_numpy(W.make_model_linear(0, i).W).cuda() for i in range(len(specs))]  # shared by layers
+    rots, xs = {}, {}
+    for l in range(nl):
+        for i in range(len(specs)):
+            Li = W.make_model_linear(l, i, with_weights=False)
+            rots[(l, i)] = rl.paro_rotation_prepare(Li.pairs, Li.theta, Li.scale)
+            xs[(l, i)] = torch.from_numpy(Li.x).cuda()
+    packed = {k: (torch.empty((specs[k[1]].N, specs[k[1]].D // 2), dtype=torch.uint8, device="cuda"),
+                  torch.empty((specs[k[1]].N, specs[k[1]].D // 128), dtype=torch.float16, device="cuda"),
+                  torch.empty((specs[k[1]].N, specs[k[1]].D // 128), dtype=torch.float16, device="cuda"))
+              for k in rots}
+    for i in range(len(specs)):  # warm the pack kernel on every shape
+        rl.paro_pack_weights(rots[(0, i)], Ws[i], out=packed[(0, i)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for (l, i), rot in rots.items():
+        rl.paro_pack_weights(rot, Ws[i], out=packed[(l, i)])
+    e1.record()
+    torch.cuda.synchronize()
+    ms_pack = e0.elapsed_time(e1)
+    n_w = nl * sum(sp.N * sp.D for sp in specs)
+    res["model_build_pack"] = {"linears": len(rots), "weights": n_w, "ms": round(ms_pack, 2),
+                               "Gweights/s": round(n_w / (ms_pack * 1e-3) / 1e9, 3),
+                               "fp16_in_GB/s": round(2 * n_w / (ms_pack * 1e-3) / 1e9, 2),
+                               "packed_bytes": sum(sum(t.numel() * t.element_size() for t in w) for w in packed.values())}
+    del Ws
+    ys = {k: torch.empty((1, specs[k[1]].N), dtype=torch.float16, device="cuda") for k in rots}
+    keys = list(rots)
+    bytes_r = sum(workload_bytes(1, specs[i].D, specs[i].N, specs[i].K) for (l, i) in keys)
+    bytes_p = sum(workload_bytes(1, specs[i].D, specs[i].N, specs[i].K, rotated=False) for (l, i) in keys)
+
+    def calls(ks, rotated):
+        return [(rots[k] if rotated else None, xs[k], *packed[k]) for k in ks]
+
+    grouped = {r: calls(keys, r) for r in (True, False)}
+    phases = {r: [calls([(l, i) for i in ph], r) for l in range(nl) for ph in W.MODEL_PHASES] for r in (True, False)}
+    ys_all = [ys[k] for k in keys]
+    ys_ph = [[ys[(l, i)] for i in ph] for l in range(nl) for ph in W.MODEL_PHASES]
+
+    def run_grouped(rotated):
+        rl.paro_linear_batch(grouped[rotated], outs=ys_all)
+
+    def run_layered(rotated):
+        for c, o in zip(phases[rotated], ys_ph):
+            rl.paro_linear_batch(c, outs=o)
+
+    for name, fn in (("grouped", run_grouped), ("layered", run_layered)):
+        ms_r = time_slots(torch, lambda s: fn(True), 2, 1, 10, 2)
+        ms_p = time_slots(torch, lambda s: fn(False), 2, 1, 10, 2)
+        gbs = bytes_r / (ms_r * 1e-3) / 1e9
+        res[f"model_decode_M1_{name}"] = {
+            "GB/s": round(gbs, 2), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "us": round(ms_r * 1e3, 2),
+            "algorithmic_bytes": bytes_r, "plain_us": round(ms_p * 1e3, 2),
+            "plain_GB/s": round(bytes_p / (ms_p * 1e-3) / 1e9, 2),
+            "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2),
+            "launch": "one paro_linear_batch call for all 196 linears" if name == "grouped" else
+                      "4 paro_linear_batch calls per layer (q/k/v, o, gate/up, down), 112 per step"}
     return res
 
 

@@ -373,6 +373,21 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     }
     if (hipError_t e = launch_rotate_batch(jobs.data(), int(jobs.size()), true, st)) return from_hip(e);
   }
+  // decode-shaped linears whose transform just ran in a batch (D or K beyond what the decode
+  // kernel runs inside): one decode launch per D on the transformed x, as for the plain calls
+  for (int i = 0; i < count; ++i) {
+    if (done[i] || !rotated[i] || !decode_takes(-1, calls[i].M, calls[i].D, calls[i].N)) continue;
+    std::vector<DecodeCall> group;
+    for (int j = i; j < count; ++j) {
+      const paro_linear_args& c = calls[j];
+      if (done[j] || !rotated[j] || c.D != calls[i].D || !decode_takes(-1, c.M, c.D, c.N)) continue;
+      group.push_back(DecodeCall{nullptr, c.M, c.N, reinterpret_cast<const uint16_t*>(slice[j]), true, c.qweight,
+                                 static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
+                                 c.y});
+      done[j] = 1;
+    }
+    if (hipError_t e = launch_decode(calls[i].D, ydtype, group.data(), int(group.size()), st)) return from_hip(e);
+  }
   for (int i = 0; i < count; ++i) {
     if (done[i]) continue;
     const paro_linear_args& c = calls[i];

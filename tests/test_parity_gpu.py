@@ -333,6 +333,13 @@ def _single(rot, xd, w, dt):
     # ragged M, K from 0 to 12, plus plain calls in between
     [(90 + i, 17 + 3 * i, 512, 40 + i, [2, 8, 12, 0][i % 4]) for i in range(20)]
     + [(120, 33, 512, 64, None), (121, 300, 512, 96, None), (122, 300, 512, 96, 8)],
+    # 40 decode-shaped calls of one D: more units than one decode launch carries (several launches),
+    # rotated and plain mixed, M from 1 to 16
+    [(200 + i, (1, 2, 4, 16, 3)[i % 5], 512, 24 + 8 * (i % 7), 8 if i % 6 else None) for i in range(40)],
+    # decode-shaped calls whose transform runs outside the decode kernel (D > 4096, K > 8):
+    # batched transforms, then one decode launch per D over the transformed rows
+    [(300 + i, (1, 3, 16, 5)[i % 4], 4224, 40 + 16 * i, 8) for i in range(6)]
+    + [(310 + i, (2, 16)[i % 2], 512, 48, 12) for i in range(4)] + [(320, 4, 4224, 64, None)],
 ])
 def test_batch_matches_single_calls_bitwise(specs):
     C.log(f"batch of {len(specs)} calls")

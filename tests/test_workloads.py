@@ -41,3 +41,15 @@ def test_custom_shapes():
     assert c.x.shape == (5, 384) and c.W.shape == (200, 384) and c.pairs.shape == (3, 192, 2)
     z = W.custom_linear(7, 1, 256, 8, 0)
     assert z.pairs.shape == (0, 128, 2) and z.theta.shape == (0, 128)
+
+
+def test_model_stack():
+    assert W.MODEL_LAYERS == 28 and len(W.MODEL_LINEARS) == 7
+    assert sorted(i for ph in W.MODEL_PHASES for i in ph) == list(range(7))
+    a = W.make_model_linear(3, 6, with_weights=False)
+    b = W.make_model_linear(4, 6, with_weights=False)
+    assert a.x.shape == (1, 8960) and a.pairs.shape == (8, 4480, 2) and a.W.shape == (0, 8960)
+    assert not np.array_equal(a.pairs, b.pairs)  # every layer has its own transform
+    g = W.make_model_linear(0, 4)
+    assert g.W.shape == (8960, 1536) and g.x.shape == (1, 1536)
+    assert np.array_equal(W.make_model_linear(0, 4, with_weights=False).pairs, g.pairs)

@@ -167,6 +167,24 @@ def make_linear(wid: int, index: int = 0, M: int | None = None, with_weights: bo
     return LinearInputs(spec, x, W, pairs, theta, scale)
 
 
+# A Qwen2.5-1.5B-shaped decoder stack for whole-model decode and build measurements: 28 layers,
+# each with q, k, v, o (hidden 1536, GQA kv dim 256), gate and up (1536 -> 8960) and down
+# (8960 -> 1536), every linear with its own transform (K = 8).
+MODEL_LAYERS = 28
+MODEL_LINEARS = (LinearSpec("q", 1536, 1536, 8), LinearSpec("k", 1536, 256, 8),
+                 LinearSpec("v", 1536, 256, 8), LinearSpec("o", 1536, 1536, 8),
+                 LinearSpec("gate", 1536, 8960, 8), LinearSpec("up", 1536, 8960, 8),
+                 LinearSpec("down", 8960, 1536, 8))
+# the linears a decode step runs together: q/k/v read the same input, so do gate/up
+MODEL_PHASES = ((0, 1, 2), (3,), (4, 5), (6,))
+
+
+def make_model_linear(layer: int, index: int, M: int = 1, with_weights: bool = True) -> LinearInputs:
+    """Linear ``index`` of decoder layer ``layer`` of the 1.5B-shaped stack (seed: [6, layer])."""
+    ss = np.random.SeedSequence([6, layer]).spawn(len(MODEL_LINEARS))[index]
+    return make_linear(0, spec=MODEL_LINEARS[index], seed_seq=ss, M=M, with_weights=with_weights)
+
+
 def custom_linear(seed: int, M: int, D: int, N: int, K: int, x_outlier_frac=0.005,
                   w_outlier_frac=0.01) -> LinearInputs:
     """Inputs with the same distributions at arbitrary shapes (ragged tails, edge cases)."""
