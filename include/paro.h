@@ -157,7 +157,7 @@ paro_status paro_rotate(const paro_rotation* r, int M, const void* x, void* xout
  * up to 256 for the transformed x, plus, for prefill-shaped calls (M > 16), room
  * for the float32 partial sums [S][M][N] of a GEMM whose reduction over D is
  * split S ways to fill the GPU. Calls whose transform runs inside the decode
- * kernel (M <= 16, D <= 4096, K <= 8) use none of it and accept ws == NULL. */
+ * kernel (see paro_rotated_linear) use none of it and accept ws == NULL. */
 size_t paro_workspace_bytes(int M, int D, int N);
 
 /*
@@ -181,8 +181,10 @@ paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t*
  * paro_rotate (float32, rounded once to float16 as the linear's 16-bit
  * operand) immediately followed by the INT4 linear of paro_w4a16_linear, with
  * the weights packed by paro_pack_weights for the same transform. With M <= 16,
- * D <= 4096 and K <= 8 the transform runs inside the decode kernel (one launch,
- * no workspace); otherwise a transform kernel writes x' into ws, which must
+ * D <= 4096, K <= 8 and (ceil(M / 4) - 1) * (N * D / 2 + N * D / 32) <= 16 MiB
+ * (the transform runs per 4-row unit and every unit reads all the weights) the
+ * transform runs inside the decode kernel (one launch, no workspace);
+ * otherwise a transform kernel writes x' into ws, which must
  * then hold at least paro_workspace_bytes(M, D, N) bytes (else
  * PARO_EWORKSPACE; the rest of it serves the linear as above), and the linear
  * reads it, on `stream`. Arguments as in paro_w4a16_linear, with D = r->D.

@@ -585,7 +585,9 @@ bool decode_takes(int K, int M, int D, int N) {
   if (M < 1 || M > kDecodeMaxM || N < 1 || D < PARO_GROUP || D > PARO_MAX_D || D % PARO_GROUP) return false;
   // 24-bit row products and 32-bit byte offsets into the packed weights
   if (N >= (1 << 24) || size_t(N) * size_t(D / 2) >= (size_t(1) << 31)) return false;
-  return K < 0 || (D <= kDecodeFusedMaxD && K <= kUnrolledStages);
+  if (K < 0) return true;
+  const size_t weight_bytes = size_t(N) * size_t(D / 2) + size_t(N) * size_t(D / PARO_GROUP) * 4;
+  return D <= kDecodeFusedMaxD && K <= kUnrolledStages && size_t((M + 3) / 4 - 1) * weight_bytes <= kDecodeFusedMaxExtraBytes;
 }
 
 hipError_t launch_decode(int D, int ydtype, const DecodeCall* calls, int count, hipStream_t st) {

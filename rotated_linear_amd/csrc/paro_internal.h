@@ -67,6 +67,11 @@ bool schedule_stage(int D, std::vector<StagePair>& pairs);
 constexpr int kDecodeMaxM = 16;
 // Largest D for which the transform runs inside the decode kernel.
 constexpr int kDecodeFusedMaxD = 4096;
+// With the transform inside, a call runs as units of up to 4 rows and every unit streams all
+// of the call's weights. Past this many extra weight bytes (units - 1 times the packed weights,
+// scales and zeros) the transform runs as its own launch and the linear as 16-row units: on
+// MI355X the extra launch costs about 6.5 us, what 16 MB of extra weight reads cost.
+constexpr size_t kDecodeFusedMaxExtraBytes = size_t(16) << 20;
 // Threads of a decode workgroup (one workgroup per CU).
 constexpr int kDecodeThreads = 512;
 // Units (row blocks of calls) and workgroups one decode launch carries in its kernel arguments.

@@ -246,6 +246,26 @@ def test_identity_transform_matches_plain_linear(M):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def test_inside_and_separate_transform_agree():
+    """A call whose later 4-row units would re-read too many weights runs its transform as its
+    own launch (M = 16, 10 MB of weights here); a 4-row call on the same weights runs it inside
+    the decode kernel. Both paths round x' once to float16 and sum in the same order, so the
+    first 4 rows agree bit for bit; the 16-row call also meets the oracle bar."""
+    L = W.custom_linear(43, 16, 1536, 12000, 8)
+    C.log("transform inside vs separate launch, D=1536 N=12000")
+    rot = _rot(L)
+    qw, sc, z = rl.paro_pack_weights(rot, C.dev(L.W, torch))
+    xd = C.dev(L.x, torch)
+    for dt in (torch.float16, torch.float32):
+        a = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z, out_dtype=dt))
+        b = C.host(rl.paro_rotated_linear(rot, xd[:4].contiguous(), qw, sc, z, out_dtype=dt))
+        assert np.array_equal(a[:4].view(np.uint8), b.view(np.uint8))
+    deq = O.dequantize(*(C.host(t) for t in (qw, sc, z)))
+    ref = O.f16_rne(O.transform_activations(L.x, L.pairs, L.theta, L.scale)).astype(np.float64) @ deq.T
+    mx, rel = C.linear_metrics(a, ref)
+    assert mx <= C.MAX_ABS and rel <= C.REL_L2, (mx, rel)
+
+
 def test_split_reduction_and_fallback():
     """M = 64: with a workspace the reduction over D is split and the float32 partial sums are
     added in split order; without one the call does not split. Both match the oracle, the
