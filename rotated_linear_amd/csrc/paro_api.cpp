@@ -62,6 +62,16 @@ paro_status check_linear_args(int M, int D, int N, const void* x, const uint8_t*
   return PARO_OK;
 }
 
+// Whether the workspace [ws, ws + need) overlaps any operand of a linear (it is written).
+bool ws_overlaps(const void* ws, size_t need, int M, int D, int N, const void* x, const uint8_t* qweight,
+                 const void* scales, const void* zeros, const void* y, int ydtype) {
+  const size_t G = size_t(D / PARO_GROUP);
+  return overlap(ws, need, x, size_t(M) * D * 2) ||
+         overlap(ws, need, y, size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2)) ||
+         overlap(ws, need, qweight, size_t(N) * D / 2) || overlap(ws, need, scales, size_t(N) * G * 2) ||
+         overlap(ws, need, zeros, size_t(N) * G * 2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,11 +240,7 @@ paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t*
   if (!ws) ws_bytes = 0;
   if (need && ws_bytes >= need) {  // room for the split partial sums: they must not overlap any operand
     if (!aligned16(ws)) return PARO_EINVAL;
-    const size_t G = size_t(D / PARO_GROUP);
-    if (overlap(ws, need, x, size_t(M) * D * 2) || overlap(ws, need, y, size_t(M) * size_t(N) * (ydtype ? 4 : 2)) ||
-        overlap(ws, need, qweight, size_t(N) * D / 2) || overlap(ws, need, scales, size_t(N) * G * 2) ||
-        overlap(ws, need, zeros, size_t(N) * G * 2))
-      return PARO_EINVAL;
+    if (ws_overlaps(ws, need, M, D, N, x, qweight, scales, zeros, y, ydtype)) return PARO_EINVAL;
   }
   return run_linear(M, D, N, static_cast<const uint16_t*>(x), false, qweight, static_cast<const uint16_t*>(scales),
                     static_cast<const uint16_t*>(zeros), y, ydtype, ws, ws_bytes, static_cast<hipStream_t>(stream));
@@ -259,8 +265,9 @@ paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void
   const size_t need = rotated_ws_bytes(R.K, M, D, N);
   if (!ws || ws_bytes < need) return PARO_EWORKSPACE;
   if (!aligned16(ws)) return PARO_EINVAL;
-  const size_t ybytes = size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2);
-  if (overlap(ws, need, x, size_t(M) * D * 2) || overlap(ws, need, y, ybytes)) return PARO_EINVAL;
+  if (ws_overlaps(ws, need, M, D, N, x, qweight, scales, zeros, y, ydtype) ||
+      overlap(ws, need, r->dev, desc_layout(r->K, D).total))
+    return PARO_EINVAL;
   return run_rotated_two_step(R, M, N, xh, qweight, sc, zr, y, ydtype, ws, need, st);
 }
 
@@ -320,7 +327,8 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     for (int i = 0; i < count; ++i) {
       const paro_linear_args& c = calls[i];
       if (c.M == 0 || c.N == 0) continue;
-      if (overlap(ws, need, c.x, size_t(c.M) * c.D * 2) || overlap(ws, need, c.y, size_t(c.M) * size_t(c.N) * ysz))
+      if (ws_overlaps(ws, need, c.M, c.D, c.N, c.x, c.qweight, c.scales, c.zeros, c.y, ydtype) ||
+          (c.rot && overlap(ws, need, c.rot->dev, desc_layout(c.rot->K, c.rot->D).total)))
         return PARO_EINVAL;
     }
   }

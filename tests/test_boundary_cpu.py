@@ -154,6 +154,14 @@ def test_calls_reject_bad_arguments_before_launch():
     assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, None, 0, None) == 5
     assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, v(FAKE * 6), 100, None) == 5
     assert lib.paro_rotated_linear(None, 1, 512, *args, v(FAKE * 5), 0, None, 0, None) == 1
+    # the workspace is written: it may overlap no operand and not the descriptor
+    need = rl.paro_workspace_bytes(64, 4096, 512)
+    assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, v(FAKE * 2), need, None) == 1
+    assert lib.paro_rotated_linear(ctypes.byref(big), 64, 512, *args, v(FAKE * 5), 0, v(FAKE * 4), need, None) == 1
+    far = _rot(8, 4096, FAKE * 40)
+    assert lib.paro_rotated_linear(ctypes.byref(far), 64, 512, *args, v(FAKE * 5), 0, v(FAKE * 40), need, None) == 1
+    plain_need = rl.paro_workspace_bytes(64, 4096, 512) - 64 * 4096 * 2
+    assert lib.paro_w4a16_linear(64, 4096, 512, *args, v(FAKE * 5), 0, v(FAKE * 3), plain_need, None) == 1
 
 
 def _call(rot, M, D, N, base):
@@ -195,6 +203,10 @@ def test_batch_rejects_bad_arguments_before_launch():
     assert lib.paro_linear_batch(2, a, 0, None, 0, None) == 5
     assert lib.paro_linear_batch(2, a, 0, ctypes.c_void_p(FAKE * 12), need - 1, None) == 5
     assert lib.paro_linear_batch(2, a, 0, ctypes.c_void_p(FAKE * 4), need, None) == 1  # workspace overlaps x
+    wq = a[1].qweight  # ... or another call's packed weights, or a transform's descriptor
+    assert lib.paro_linear_batch(2, a, 0, ctypes.c_void_p(wq), need, None) == 1
+    a = Arr(_call(_rot(12, 256, FAKE * 30), 4, 256, 64, 4), _call(ok, 4, 256, 64, 8))
+    assert lib.paro_linear_batch(2, a, 0, ctypes.c_void_p(FAKE * 30), need, None) == 1
     big = _rot(8, 4096)
     a = Arr(_call(big, 64, 4096, 64, 4))
     need = lib.paro_linear_batch_workspace_bytes(1, a)
