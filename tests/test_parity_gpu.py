@@ -360,6 +360,9 @@ def _single(rot, xd, w, dt):
     # batched transforms, then one decode launch per D over the transformed rows
     [(300 + i, (1, 3, 16, 5)[i % 4], 4224, 40 + 16 * i, 8) for i in range(6)]
     + [(310 + i, (2, 16)[i % 2], 512, 48, 12) for i in range(4)] + [(320, 4, 4224, 64, None)],
+    # one layer of the 1.5B-shaped stack at decode M = 1 (q, k, v, o, gate, up, down), as the
+    # whole-stack decode step batches it
+    [(400 + i, 1, s.D, s.N, s.K) for i, s in enumerate(W.MODEL_LINEARS)],
 ])
 def test_batch_matches_single_calls_bitwise(specs):
     C.log(f"batch of {len(specs)} calls")
