@@ -478,7 +478,67 @@ def extras(rl, torch, W, args):
     res.update(layer8b(rl, torch, W, args))
     res.update(overhead_vs_k(rl, torch, W, args))
     res.update(model_stack(rl, torch, W, args))
+    res.update(prefill_overlap(rl, torch, W, args))
     return res
+
+
+def prefill_overlap(rl, torch, W, args):
+    """The down_proj prefill (M = 2048) with its rows in C chunks: chunk c + 1 is transformed on a
+    second stream while the plain INT4 linear runs on chunk c (paro_rotate, then
+    paro_w4a16_linear on the transformed rows; events order each chunk's two steps). Beside it,
+    the same chunks one after the other on one stream, and the unchunked fused call. Each variant
+    is one HIP graph per step."""
+    L4 = Linear(rl, torch, W.make_linear(4, 0))
+    M, D, N = 2048, L4.D, L4.N
+    x = torch.from_numpy(L4.L.x[:M]).cuda()
+    xr = torch.empty_like(x)
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    flops = 2.0 * M * D * N
+    entry = {}
+    st = Step(rl, torch, [L4], [M])
+    ms_f = time_slots(torch, lambda s: st.enqueue(s), 4, 4, 20, 4)
+    entry["fused_call_us"] = round(ms_f * 1e3, 2)
+    side = torch.cuda.Stream()
+    for C in (1, 2, 4, 8):
+        rows = M // C
+        ws = [torch.empty(max(rl.paro_workspace_bytes(rows, D, N), 256), dtype=torch.uint8, device="cuda")
+              for _ in range(2)]
+
+        def chunk(c, gemm_ws):
+            r = slice(c * rows, (c + 1) * rows)
+            rl.paro_w4a16_linear(xr[r], *L4.w, out=y[r], ws=gemm_ws)
+
+        def serial(s):
+            for c in range(C):
+                r = slice(c * rows, (c + 1) * rows)
+                rl.paro_rotate(L4.rot, x[r], out=xr[r])
+                chunk(c, ws[0])
+
+        def overlapped(s):
+            main = torch.cuda.current_stream()
+            side.wait_stream(main)
+            done = []
+            for c in range(C):  # transforms on the side stream, each chunk's linear on the main one
+                r = slice(c * rows, (c + 1) * rows)
+                with torch.cuda.stream(side):
+                    rl.paro_rotate(L4.rot, x[r], out=xr[r])
+                    ev = torch.cuda.Event()
+                    ev.record(side)
+                done.append(ev)
+            for c in range(C):
+                main.wait_event(done[c])
+                chunk(c, ws[c % 2] if C > 1 else ws[0])
+            main.wait_stream(side)
+
+        ms_s = time_slots(torch, serial, 4, 4, 20, 4)
+        ms_o = time_slots(torch, overlapped, 4, 4, 20, 4) if C > 1 else ms_s
+        entry[f"C{C}"] = {"serial_us": round(ms_s * 1e3, 2), "overlapped_us": round(ms_o * 1e3, 2),
+                          "overlapped_TFLOP/s": round(flops / (ms_o * 1e-3) / 1e12, 2)}
+    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), 4, 4, 20, 4)
+    entry["plain_us"] = round(ms_p * 1e3, 2)
+    best = min(v["overlapped_us"] for k, v in entry.items() if k.startswith("C"))
+    entry["best_overhead_pct"] = round((best - ms_p * 1e3) / (ms_p * 1e3) * 100, 2)
+    return {"prefill_overlap_down_M2048": entry}
 
 
 def _with_stages(L, K):
