@@ -39,7 +39,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=1000)  # about 14 ms: the GPU clocks settle
     p.add_argument("--no-extras", action="store_true", help="skip the gate+up / down_proj extras")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -157,10 +157,17 @@ def capture(torch, fn, n_graphs):
     return graphs
 
 
-def time_graphs(torch, graphs, steps, warmup):
-    """Replay graphs[t % len] for t < steps; returns ms per step (events bracket the K steps)."""
-    for t in range(warmup):
+def time_graphs(torch, graphs, steps, warmup, min_warm_s=0.0):
+    """Replay graphs[t % len] for t < steps; returns ms per step (events bracket the K steps).
+    Before them: `warmup` untimed replays, continued until at least `min_warm_s` seconds have
+    passed (an idle GPU lowers its clocks; a few ms of work bring them back)."""
+    t0 = time.perf_counter()
+    t = 0
+    while t < warmup or time.perf_counter() - t0 < min_warm_s:
         graphs[t % len(graphs)].replay()
+        t += 1
+        if t % len(graphs) == 0 and t >= warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -172,13 +179,14 @@ def time_graphs(torch, graphs, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-def time_slots(torch, fn, n_slots, per, steps, warmup):
+def time_slots(torch, fn, n_slots, per, steps, warmup, min_warm_s=0.05):
     """fn(slot) for slot < n_slots, captured as graphs of `per` consecutive slots (so one replay
     carries several steps and host launch cost stays out of the per-step time); returns ms per
-    step over `steps` steps after `warmup` untimed ones."""
+    step over `steps` steps after `warmup` untimed ones (and at least `min_warm_s` seconds of
+    them)."""
     n_graphs = max(1, n_slots // per)
     gs = capture(torch, lambda g: [fn(g * per + r) for r in range(per)], n_graphs)
-    ms = time_graphs(torch, gs, max(1, steps // per), max(1, warmup // per)) / per
+    ms = time_graphs(torch, gs, max(1, steps // per), max(1, warmup // per), min_warm_s) / per
     del gs
     return ms
 
@@ -305,9 +313,9 @@ def main():
     per_graph = math.gcd(args.steps, 8) or 1  # steps per captured graph (divides K exactly)
     n_graphs = max(1, n_slots // per_graph)
 
-    def timed(rotated, batched):
+    def timed(rotated, batched):  # exactly --warmup untimed steps, then --steps timed ones
         return time_slots(torch, lambda s: step.enqueue(s, rotated=rotated, batched=batched), n_graphs * per_graph,
-                          per_graph, args.steps, args.warmup)
+                          per_graph, args.steps, args.warmup, min_warm_s=0.0)
 
     # the step: the 12 projections as one batched call (one launch of the decode kernel)
     ms_rot = timed(True, True)
