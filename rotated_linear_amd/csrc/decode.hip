@@ -99,8 +99,6 @@ __device__ inline h8 dequant_word(uint32_t u, h2 zlo, h2 zhi, uint32_t m0, uint3
 
 // An empty statement that makes v look redefined here: code computed from v stays below it.
 __device__ inline void pin(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
-__device__ inline void pin(float4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
-__device__ inline void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 __device__ inline h8 decode_order(h8 a) { return __builtin_shufflevector(a, a, 0, 4, 1, 5, 2, 6, 3, 7); }
 

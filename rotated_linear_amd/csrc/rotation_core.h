@@ -199,8 +199,4 @@ __device__ inline void ring_run(StageRing<NT, PPT, PD, EXACT, TIGHT>& ring, floa
 template <class T>
 using gptr = __attribute__((address_space(1))) T*;
 
-// Slot of channel offset e (0..7) of an 8-channel word in the order the INT4
-// decode produces: [0, 4, 1, 5, 2, 6, 3, 7].
-__device__ inline int nib_slot(int e) { return ((e & 3) << 1) | (e >> 2); }
-
 }  // namespace paro
