@@ -321,20 +321,60 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs p) {
 }
 
 // y = sum over the S split partials [S][M][N], in split order; y rows are ldy elements apart.
+// A thread loads all S partials of its elements before adding them (the loads of one element
+// are independent: issued together they cost one memory round trip, not S), four consecutive
+// elements at a time when rows allow it (N % 4 == 0).
+template <int S, bool VEC>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, void* __restrict__ y,
-                                                            int M, int N, int ldy, int S, int ydtype) {
+                                                            int M, int N, int ldy, int ydtype) {
+  typedef float f4v __attribute__((ext_vector_type(4)));
   const size_t count = size_t(M) * size_t(N);
   const size_t stride = size_t(gridDim.x) * blockDim.x;
-  for (size_t e = size_t(blockIdx.x) * blockDim.x + threadIdx.x; e < count; e += stride) {
-    float v = part[e];
-    for (int s = 1; s < S; ++s) v += part[size_t(s) * count + e];
+  constexpr int E = VEC ? 4 : 1;
+  for (size_t e = (size_t(blockIdx.x) * blockDim.x + threadIdx.x) * E; e < count; e += stride * E) {
     const size_t m = e / size_t(N), n = e - m * size_t(N);
     const size_t o = m * size_t(ldy) + n;
-    if (ydtype == PARO_F32)
-      static_cast<float*>(y)[o] = v;
-    else
-      static_cast<_Float16*>(y)[o] = static_cast<_Float16>(v);
+    if constexpr (VEC) {
+      f4v p[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) p[s] = *reinterpret_cast<const f4v*>(part + size_t(s) * count + e);
+      f4v v = p[0];
+#pragma unroll
+      for (int s = 1; s < S; ++s) v += p[s];
+      if (ydtype == PARO_F32) {
+        *reinterpret_cast<f4v*>(static_cast<float*>(y) + o) = v;
+      } else {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 hv = {static_cast<_Float16>(v.x), static_cast<_Float16>(v.y), static_cast<_Float16>(v.z),
+                       static_cast<_Float16>(v.w)};
+        *reinterpret_cast<h4*>(static_cast<_Float16*>(y) + o) = hv;
+      }
+    } else {
+      float p[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) p[s] = part[size_t(s) * count + e];
+      float v = p[0];
+#pragma unroll
+      for (int s = 1; s < S; ++s) v += p[s];
+      if (ydtype == PARO_F32)
+        static_cast<float*>(y)[o] = v;
+      else
+        static_cast<_Float16*>(y)[o] = static_cast<_Float16>(v);
+    }
   }
+}
+
+template <int S>
+hipError_t launch_reduce(const float* part, void* y, int M, int N, int ldy, int ydtype, hipStream_t st) {
+  // 16-byte partial loads and 8- or 16-byte stores need N, ldy (and so every row start) in fours
+  const bool vec = N % 4 == 0 && ldy % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+  const size_t items = (size_t(M) * N + (vec ? 3 : 0)) / (vec ? 4 : 1);
+  const int blocks = int(std::min<size_t>((items + 255) / 256, 4096));
+  if (vec)
+    hipLaunchKernelGGL((splitk_reduce_kernel<S, true>), dim3(blocks), dim3(256), 0, st, part, y, M, N, ldy, ydtype);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<S, false>), dim3(blocks), dim3(256), 0, st, part, y, M, N, ldy, ydtype);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int PD, bool APERM>
@@ -432,11 +472,17 @@ hipError_t launch_block(int M, int D, int N, const uint16_t* x, bool x_nibble_or
   PARO_GEMM_CASE(64, 128, 2, 2)
 #undef PARO_GEMM_CASE
   if (e != hipSuccess || g.splits == 1) return e;
-  const size_t count = size_t(M) * N;
-  const int blocks = int(std::min<size_t>((count + 255) / 256, 4096));
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, static_cast<const float*>(ws), y, M, N,
-                     ldy, g.splits, ydtype);
-  return hipGetLastError();
+  const float* part = static_cast<const float*>(ws);
+  switch (g.splits) {  // the planner splits at most 8 ways
+    case 2: return launch_reduce<2>(part, y, M, N, ldy, ydtype, st);
+    case 3: return launch_reduce<3>(part, y, M, N, ldy, ydtype, st);
+    case 4: return launch_reduce<4>(part, y, M, N, ldy, ydtype, st);
+    case 5: return launch_reduce<5>(part, y, M, N, ldy, ydtype, st);
+    case 6: return launch_reduce<6>(part, y, M, N, ldy, ydtype, st);
+    case 7: return launch_reduce<7>(part, y, M, N, ldy, ydtype, st);
+    case 8: return launch_reduce<8>(part, y, M, N, ldy, ydtype, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
