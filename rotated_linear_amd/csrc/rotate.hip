@@ -209,10 +209,12 @@ hipError_t launch_rows(const RotJobs& J, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int NT, int R, int PPT, int PD, bool PERM>
+// PD: ring depth when the pairs divide evenly over the threads (EXACT), PDN otherwise (the
+// range checks take registers).
+template <int NT, int R, int PPT, int PD, bool PERM, int PDN = PD>
 hipError_t launch_exact(const RotJobs& J, int grid, hipStream_t st) {
   if (J.D / 2 == PPT * NT) return launch_rows<NT, R, PPT, PD, true, PERM>(J, grid, st);
-  return launch_rows<NT, R, PPT, PD, false, PERM>(J, grid, st);
+  return launch_rows<NT, R, PPT, PDN, false, PERM>(J, grid, st);
 }
 
 // Threads, pairs per thread per stage (PPT) and ring depth by row width (the ring is shallower
@@ -227,8 +229,10 @@ hipError_t launch_ppt(const RotJobs& J, int grid, hipStream_t st) {
   if (P <= 3072) return launch_exact<512, R, 6, 2, PERM>(J, grid, st);
   if (P <= 4608) return launch_exact<512, R, 9, 2, PERM>(J, grid, st);
   if constexpr (R <= 2) {  // wider rows (D > 9216) never take 4 rows per workgroup
-    if (P <= 6144) return launch_exact<512, R, 12, 2, PERM>(J, grid, st);
-    if (P <= 7168) return launch_exact<512, R, 14, 1, PERM>(J, grid, st);
+    // two stages of records in flight where the registers allow it (no spills): one stage
+    // leaves every stage waiting for its records' round trip
+    if (P <= 6144) return launch_exact<512, R, 12, 2, PERM, (R == 1 ? 2 : 1)>(J, grid, st);
+    if (P <= 7168) return launch_exact<512, R, 14, 2, PERM, (R == 1 ? 2 : 1)>(J, grid, st);
     return launch_exact<512, R, 16, 1, PERM>(J, grid, st);
   }
   return hipErrorInvalidValue;
