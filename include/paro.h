@@ -219,8 +219,10 @@ size_t paro_linear_batch_workspace_bytes(int count, const paro_linear_args* call
  * transforms of the calls with M <= 256 that share D run as one launch (or as
  * few as the GPU holds at once); the decode-shaped ones among them (M <= 16,
  * with D or K past what the decode kernel runs inside) then run their linears
- * as one decode launch per D, the others one after the other (a longer
- * call's transform right before its linear), each call using its own
+ * as one decode launch per D; the GEMM-shaped linears of up to 256 rows that
+ * share a tiling run as one launch (and their split reductions as one more),
+ * longer calls one at a time (a rotated one's transform right before its
+ * linear); each call uses its own
  * consecutive slice of ws (ws_bytes >= paro_linear_batch_workspace_bytes). The calls may run concurrently, so no
  * call's y may overlap any buffer of another call (PARO_EINVAL); every call is
  * checked as its single call would be before anything is enqueued. The

@@ -33,6 +33,9 @@
 //   * optional split-K: split s of S takes a contiguous range of groups and writes float32
 //     partial sums; a second kernel adds the S partials in order (deterministic).
 #include <algorithm>
+#include <string.h>
+
+#include <vector>
 
 #include "paro_internal.h"
 
@@ -119,8 +122,10 @@ struct Stage {
   uint32_t s, z;
 };
 
+// One workgroup's tile of one call; b is the workgroup's index among the call's workgroups
+// (b % 8 must be the XCD the workgroup runs on).
 template <int BM, int BN, int WM, int PD, bool APERM>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs p) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int b) {
   using T = Tile<BM, BN, WM>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs p) {
 
   // ---- workgroup -> (split, tile): XCD ranges, then column groups of kGroupM tile rows
   const int W = p.tiles_m * p.tiles_n * p.splits;
-  const int b = blockIdx.x, xcd = b % kXcds;
+  const int xcd = b % kXcds;
   const int w = xcd * (W / kXcds) + min(xcd, W % kXcds) + b / kXcds;
   const int T_ = p.tiles_m * p.tiles_n;
   const int split = w / T_, t = w - split * T_;
@@ -320,18 +325,43 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs p) {
   }
 }
 
+template <int BM, int BN, int WM, int PD, bool APERM>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs p) {
+  gemm_tile<BM, BN, WM, PD, APERM>(p, int(blockIdx.x));
+}
+
+// Several independent calls with the same tiling in one launch: call i owns workgroups
+// [block0[i], block0[i] + tiles * splits), block0[i] a multiple of 8 (so a workgroup's index
+// within its call keeps its XCD); the workgroups in the gaps end at once.
+struct GemmGroupArgs {
+  GemmArgs p[kGemmGroupMax];
+  int block0[kGemmGroupMax];
+  int n;
+};
+
+template <int BM, int BN, int WM, int PD, bool APERM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_group_kernel(
+    const GemmGroupArgs g) {
+  const int blk = int(blockIdx.x);
+  int i = 0;
+  while (i + 1 < g.n && blk >= g.block0[i + 1]) ++i;
+  const GemmArgs& p = g.p[i];
+  const int b = blk - g.block0[i];
+  if (b >= p.tiles_m * p.tiles_n * p.splits) return;  // uniform: the whole workgroup
+  gemm_tile<BM, BN, WM, PD, APERM>(p, b);
+}
+
 // y = sum over the S split partials [S][M][N], in split order; y rows are ldy elements apart.
 // A thread loads all S partials of its elements before adding them (the loads of one element
 // are independent: issued together they cost one memory round trip, not S), four consecutive
-// elements at a time when rows allow it (N % 4 == 0).
+// elements at a time when rows allow it (N % 4 == 0). Items item0, item0 + stride, ...
 template <int S, bool VEC>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, void* __restrict__ y,
-                                                            int M, int N, int ldy, int ydtype) {
+__device__ __forceinline__ void reduce_items(const float* __restrict__ part, void* __restrict__ y, int M, int N,
+                                             int ldy, int ydtype, size_t item0, size_t stride) {
   typedef float f4v __attribute__((ext_vector_type(4)));
   const size_t count = size_t(M) * size_t(N);
-  const size_t stride = size_t(gridDim.x) * blockDim.x;
   constexpr int E = VEC ? 4 : 1;
-  for (size_t e = (size_t(blockIdx.x) * blockDim.x + threadIdx.x) * E; e < count; e += stride * E) {
+  for (size_t e = item0 * E; e < count; e += stride * E) {
     const size_t m = e / size_t(N), n = e - m * size_t(N);
     const size_t o = m * size_t(ldy) + n;
     if constexpr (VEC) {
@@ -364,17 +394,69 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-template <int S>
-hipError_t launch_reduce(const float* part, void* y, int M, int N, int ldy, int ydtype, hipStream_t st) {
+template <bool VEC>
+__device__ __forceinline__ void reduce_any(int S, const float* part, void* y, int M, int N, int ldy, int ydtype,
+                                           size_t item0, size_t stride) {
+  switch (S) {  // the planner splits at most 8 ways
+    case 2: reduce_items<2, VEC>(part, y, M, N, ldy, ydtype, item0, stride); break;
+    case 3: reduce_items<3, VEC>(part, y, M, N, ldy, ydtype, item0, stride); break;
+    case 4: reduce_items<4, VEC>(part, y, M, N, ldy, ydtype, item0, stride); break;
+    case 5: reduce_items<5, VEC>(part, y, M, N, ldy, ydtype, item0, stride); break;
+    case 6: reduce_items<6, VEC>(part, y, M, N, ldy, ydtype, item0, stride); break;
+    case 7: reduce_items<7, VEC>(part, y, M, N, ldy, ydtype, item0, stride); break;
+    default: reduce_items<8, VEC>(part, y, M, N, ldy, ydtype, item0, stride); break;
+  }
+}
+
+// One reduction per launch (S uniform) or several, one per call of a group (each block
+// serves one call; S and the vector width are uniform per block).
+struct ReduceCall {
+  const float* part;
+  void* y;
+  int M, N, ldy, S, vec, blocks;
+};
+struct ReduceGroupArgs {
+  ReduceCall c[kGemmGroupMax];
+  int block0[kGemmGroupMax];
+  int n, ydtype;
+};
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceGroupArgs g) {
+  const int blk = int(blockIdx.x);
+  int i = 0;
+  while (i + 1 < g.n && blk >= g.block0[i + 1]) ++i;
+  const ReduceCall& c = g.c[i];
+  const size_t item0 = size_t(blk - g.block0[i]) * 256 + threadIdx.x, stride = size_t(c.blocks) * 256;
+  if (c.vec)
+    reduce_any<true>(c.S, c.part, c.y, c.M, c.N, c.ldy, g.ydtype, item0, stride);
+  else
+    reduce_any<false>(c.S, c.part, c.y, c.M, c.N, c.ldy, g.ydtype, item0, stride);
+}
+
+ReduceCall reduce_call(const float* part, void* y, int M, int N, int ldy, int S) {
   // 16-byte partial loads and 8- or 16-byte stores need N, ldy (and so every row start) in fours
   const bool vec = N % 4 == 0 && ldy % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
   const size_t items = (size_t(M) * N + (vec ? 3 : 0)) / (vec ? 4 : 1);
   const int blocks = int(std::min<size_t>((items + 255) / 256, 4096));
-  if (vec)
-    hipLaunchKernelGGL((splitk_reduce_kernel<S, true>), dim3(blocks), dim3(256), 0, st, part, y, M, N, ldy, ydtype);
-  else
-    hipLaunchKernelGGL((splitk_reduce_kernel<S, false>), dim3(blocks), dim3(256), 0, st, part, y, M, N, ldy, ydtype);
-  return hipGetLastError();
+  return ReduceCall{part, y, M, N, ldy, S, vec ? 1 : 0, blocks};
+}
+
+hipError_t launch_reduce_group(const ReduceCall* calls, int n, int ydtype, hipStream_t st) {
+  for (int i0 = 0; i0 < n; i0 += kGemmGroupMax) {
+    ReduceGroupArgs g;
+    memset(&g, 0, sizeof(g));
+    g.n = std::min(n - i0, kGemmGroupMax);
+    g.ydtype = ydtype;
+    int grid = 0;
+    for (int i = 0; i < g.n; ++i) {
+      g.c[i] = calls[i0 + i];
+      g.block0[i] = grid;
+      grid += g.c[i].blocks;
+    }
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, st, g);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
 }
 
 template <int BM, int BN, int WM, int PD, bool APERM>
@@ -436,10 +518,11 @@ namespace {
 
 // One launch over rows [0, M) and columns [0, N) of the operands as given (y rows ldy apart);
 // the caller keeps every byte offset of the kernel below 4 GiB.
-hipError_t launch_block(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
-                        const uint16_t* scales, const uint16_t* zeros, void* y, int ldy, int ydtype, void* ws,
-                        size_t ws_bytes, hipStream_t st) {
-  GemmPlan g = plan_gemm(M, D, N);
+// The plan and kernel arguments of one call over rows [0, M) and columns [0, N) of the operands
+// as given (y rows ldy apart); no split without room for the partial sums in ws.
+GemmArgs make_args(int M, int D, int N, const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
+                   const uint16_t* zeros, void* y, int ldy, int ydtype, void* ws, size_t ws_bytes, GemmPlan& g) {
+  g = plan_gemm(M, D, N);
   if (g.splits > 1 && ws_bytes < size_t(g.splits) * M * N * 4) g.splits = 1;  // no room for partials
   GemmArgs a;
   a.x = x;
@@ -458,10 +541,31 @@ hipError_t launch_block(int M, int D, int N, const uint16_t* x, bool x_nibble_or
   a.gps = (a.G + g.splits - 1) / g.splits;
   a.ydtype = ydtype;
   a.ldy = ldy;
-  hipError_t e = hipErrorInvalidValue;
-#define PARO_GEMM_CASE(bm, bn, wm, pd)                                                                      \
-  if (g.BM == bm && g.BN == bn && g.WM == wm && g.PD == pd)                                                 \
-    e = x_nibble_order ? launch_tile<bm, bn, wm, pd, true>(a, st) : launch_tile<bm, bn, wm, pd, false>(a, st);
+  return a;
+}
+
+template <int BM, int BN, int WM, int PD, bool APERM>
+hipError_t launch_group_tile(const GemmGroupArgs& ga, int grid, hipStream_t st) {
+  using T = Tile<BM, BN, WM>;
+  const void* fn = reinterpret_cast<const void*>(&gemm_group_kernel<BM, BN, WM, PD, APERM>);
+  if (T::LDS > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(T::LDS));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, PD, APERM>), dim3(grid), dim3(kThreads), T::LDS, st, ga);
+  return hipGetLastError();
+}
+
+// The tile kernel of plan g: one call (ga == nullptr: a) or a group of calls sharing g.
+hipError_t dispatch(const GemmPlan& g, bool x_nibble_order, const GemmArgs& a, const GemmGroupArgs* ga, int grid,
+                    hipStream_t st) {
+#define PARO_GEMM_CASE(bm, bn, wm, pd)                                                                         \
+  if (g.BM == bm && g.BN == bn && g.WM == wm && g.PD == pd) {                                                  \
+    if (ga)                                                                                                    \
+      return x_nibble_order ? launch_group_tile<bm, bn, wm, pd, true>(*ga, grid, st)                           \
+                            : launch_group_tile<bm, bn, wm, pd, false>(*ga, grid, st);                         \
+    return x_nibble_order ? launch_tile<bm, bn, wm, pd, true>(a, st) : launch_tile<bm, bn, wm, pd, false>(a, st); \
+  }
   PARO_GEMM_CASE(128, 256, 1, 2)
   PARO_GEMM_CASE(128, 128, 1, 2)
   PARO_GEMM_CASE(64, 256, 1, 2)
@@ -471,18 +575,24 @@ hipError_t launch_block(int M, int D, int N, const uint16_t* x, bool x_nibble_or
   PARO_GEMM_CASE(64, 192, 2, 2)
   PARO_GEMM_CASE(64, 128, 2, 2)
 #undef PARO_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_block(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, void* y, int ldy, int ydtype, void* ws,
+                        size_t ws_bytes, hipStream_t st) {
+  GemmPlan g;
+  const GemmArgs a = make_args(M, D, N, x, qweight, scales, zeros, y, ldy, ydtype, ws, ws_bytes, g);
+  hipError_t e = dispatch(g, x_nibble_order, a, nullptr, 0, st);
   if (e != hipSuccess || g.splits == 1) return e;
-  const float* part = static_cast<const float*>(ws);
-  switch (g.splits) {  // the planner splits at most 8 ways
-    case 2: return launch_reduce<2>(part, y, M, N, ldy, ydtype, st);
-    case 3: return launch_reduce<3>(part, y, M, N, ldy, ydtype, st);
-    case 4: return launch_reduce<4>(part, y, M, N, ldy, ydtype, st);
-    case 5: return launch_reduce<5>(part, y, M, N, ldy, ydtype, st);
-    case 6: return launch_reduce<6>(part, y, M, N, ldy, ydtype, st);
-    case 7: return launch_reduce<7>(part, y, M, N, ldy, ydtype, st);
-    case 8: return launch_reduce<8>(part, y, M, N, ldy, ydtype, st);
-    default: return hipErrorInvalidValue;
-  }
+  const ReduceCall r = reduce_call(static_cast<const float*>(ws), y, M, N, ldy, g.splits);
+  return launch_reduce_group(&r, 1, ydtype, st);
+}
+
+// Whether the kernel's 32-bit byte offsets cover the call in one block (see launch_gemm).
+bool fits_one_block(int M, int D, int N) {
+  const size_t lim = (size_t(1) << 32) - 1;
+  return size_t(M) <= lim / (size_t(D) * 2) / 256 * 256 && size_t(N) <= lim / (size_t(D) / 2) / 256 * 256;
 }
 
 }  // namespace
@@ -506,6 +616,55 @@ hipError_t launch_gemm(int M, int D, int N, const uint16_t* x, bool x_nibble_ord
       if (e != hipSuccess) return e;
     }
   return hipSuccess;
+}
+
+hipError_t launch_gemm_group(const GemmCall* calls, int n, int ydtype, hipStream_t st) {
+  struct Item {
+    GemmPlan g;
+    GemmArgs a;
+    bool nib;
+  };
+  std::vector<Item> items;
+  std::vector<ReduceCall> reduces;
+  for (int i = 0; i < n; ++i) {
+    const GemmCall& c = calls[i];
+    if (c.M <= 0 || c.N <= 0) continue;
+    if (!fits_one_block(c.M, c.D, c.N)) {  // blocks of rows and columns, one call at a time
+      if (hipError_t e = launch_gemm(c.M, c.D, c.N, c.x, c.x_nibble_order, c.qweight, c.scales, c.zeros, c.y, ydtype,
+                                     c.ws, c.ws_bytes, st))
+        return e;
+      continue;
+    }
+    Item it;
+    it.a = make_args(c.M, c.D, c.N, c.x, c.qweight, c.scales, c.zeros, c.y, c.N, ydtype, c.ws, c.ws_bytes, it.g);
+    it.nib = c.x_nibble_order;
+    items.push_back(it);
+    if (it.g.splits > 1)
+      reduces.push_back(reduce_call(static_cast<const float*>(c.ws), c.y, c.M, c.N, c.N, it.g.splits));
+  }
+  // calls with the same tiling and x order share launches (at most kGemmGroupMax each)
+  std::vector<char> done(items.size(), 0);
+  for (size_t i = 0; i < items.size(); ++i) {
+    if (done[i]) continue;
+    GemmGroupArgs ga;
+    memset(&ga, 0, sizeof(ga));
+    int grid = 0;
+    for (size_t j = i; j < items.size() && ga.n < kGemmGroupMax; ++j) {
+      const Item& b = items[j];
+      if (done[j] || b.nib != items[i].nib || b.g.BM != items[i].g.BM || b.g.BN != items[i].g.BN ||
+          b.g.WM != items[i].g.WM || b.g.PD != items[i].g.PD)
+        continue;
+      grid = (grid + kXcds - 1) / kXcds * kXcds;  // every call starts on XCD 0
+      ga.p[ga.n] = b.a;
+      ga.block0[ga.n] = grid;
+      grid += b.a.tiles_m * b.a.tiles_n * b.a.splits;
+      ++ga.n;
+      done[j] = 1;
+    }
+    if (hipError_t e = dispatch(items[i].g, items[i].nib, items[i].a, &ga, grid, st)) return e;
+  }
+  if (reduces.empty()) return hipSuccess;
+  return launch_reduce_group(reduces.data(), int(reduces.size()), ydtype, st);
 }
 
 }  // namespace paro

@@ -358,8 +358,8 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
   }
   // the rest: every call owns a consecutive slice of ws (for a rotated call: its transformed x,
   // then its linear's partial sums). The transforms of the short calls (M <= 256) that share D
-  // run as one batched launch, then the linears one after the other; a long call's transform
-  // runs right before its linear, whose x' is then still in the caches.
+  // run as one batched launch, then the linears in as few launches as their shapes allow; a long
+  // call's transform runs right before its linear, whose x' is then still in the caches.
   std::vector<char*> slice(size_t(count > 0 ? count : 0), nullptr);
   char* wsp = static_cast<char*>(ws);
   for (int i = 0; i < count; ++i) {
@@ -396,28 +396,50 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     }
     if (hipError_t e = launch_decode(calls[i].D, ydtype, group.data(), int(group.size()), st)) return from_hip(e);
   }
+  // GEMM-shaped linears of up to 256 rows, on x or on an already transformed x: the calls
+  // sharing a tiling run in one launch, their split reductions in one more (one such call
+  // rarely fills the GPU; larger ones do, and run one at a time below)
+  std::vector<GemmCall> gemms;
+  for (int i = 0; i < count; ++i) {
+    if (done[i] || (calls[i].rot && !rotated[i]) || calls[i].M > kBatchTransformMaxM) continue;
+    const paro_linear_args& c = calls[i];
+    GemmCall g{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
+               static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
+               linear_ws_bytes(c.M, c.D, c.N)};
+    if (c.rot) {
+      const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
+      g.x = reinterpret_cast<const uint16_t*>(slice[i]);
+      g.x_nibble_order = true;
+      g.ws = slice[i] + xr_bytes;
+      g.ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+    }
+    gemms.push_back(g);
+    done[i] = 1;
+  }
+  if (!gemms.empty())
+    if (hipError_t e = launch_gemm_group(gemms.data(), int(gemms.size()), ydtype, st)) return from_hip(e);
+  // the longer calls one at a time, a rotated call's transform right before its linear, whose
+  // x' is then still in the caches
   for (int i = 0; i < count; ++i) {
     if (done[i]) continue;
     const paro_linear_args& c = calls[i];
-    const uint16_t* sc = static_cast<const uint16_t*>(c.scales);
-    const uint16_t* zr = static_cast<const uint16_t*>(c.zeros);
-    paro_status s;
-    if (c.rot) {
-      const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
-      const size_t part = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
-      if (!rotated[i]) {
-        rots[i] = dev_rot(*c.rot);
-        if (hipError_t e = launch_rotate(rots[i], c.M, static_cast<const uint16_t*>(c.x),
-                                         reinterpret_cast<uint16_t*>(slice[i]), true, st))
-          return from_hip(e);
-      }
-      s = run_linear(c.M, c.D, c.N, reinterpret_cast<const uint16_t*>(slice[i]), true, c.qweight, sc, zr, c.y,
-                     ydtype, slice[i] + xr_bytes, part, st);
-    } else {
-      s = run_linear(c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight, sc, zr, c.y, ydtype,
-                     slice[i], linear_ws_bytes(c.M, c.D, c.N), st);
+    if (!c.rot) {
+      if (paro_status s = run_linear(c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
+                                     static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
+                                     c.y, ydtype, slice[i], linear_ws_bytes(c.M, c.D, c.N), st))
+        return s;
+      continue;
     }
-    if (s != PARO_OK) return s;
+    const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
+    const size_t part = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+    rots[i] = dev_rot(*c.rot);
+    if (hipError_t e = launch_rotate(rots[i], c.M, static_cast<const uint16_t*>(c.x),
+                                     reinterpret_cast<uint16_t*>(slice[i]), true, st))
+      return from_hip(e);
+    if (paro_status s = run_linear(c.M, c.D, c.N, reinterpret_cast<const uint16_t*>(slice[i]), true, c.qweight,
+                                   static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
+                                   c.y, ydtype, slice[i] + xr_bytes, part, st))
+      return s;
   }
   return PARO_OK;
 }

@@ -127,6 +127,8 @@ hipError_t launch_rotate(const DevRot& R, int M, const uint16_t* x, uint16_t* xo
 // Several transforms of the same D (each with its own descriptor, x and output) in as few
 // launches as the GPU holds at once (up to kRotMaxJobs per launch).
 constexpr int kRotMaxJobs = 16;
+// Calls one grouped GEMM (or split-reduction) launch carries in its kernel arguments.
+constexpr int kGemmGroupMax = 16;
 struct RotateJob {
   const DevRot* R;
   int M;
@@ -149,5 +151,21 @@ size_t gemm_workspace_bytes(int M, int D, int N);
 hipError_t launch_gemm(int M, int D, int N, const uint16_t* x, bool x_nibble_order, const uint8_t* qweight,
                        const uint16_t* scales, const uint16_t* zeros, void* y, int ydtype, void* ws,
                        size_t ws_bytes, hipStream_t st);
+
+// Independent GEMM-shaped calls (each as launch_gemm would run it, bit for bit: same tiling,
+// same split, same summation order): the calls sharing a tiling run in one launch, and all
+// their split reductions in one more.
+struct GemmCall {
+  int M, D, N;
+  const uint16_t* x;
+  bool x_nibble_order;
+  const uint8_t* qweight;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  void* y;
+  void* ws;
+  size_t ws_bytes;
+};
+hipError_t launch_gemm_group(const GemmCall* calls, int n, int ydtype, hipStream_t st);
 
 }  // namespace paro
