@@ -244,6 +244,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int b) {
       }
     }
     const _Float16* arow = As + (wm * (BM / WM) + l32) * kLdaH + hh * 32;
+    // a wave issuing its MFMAs goes first (the other waves of the SIMD are then mostly in their
+    // load / LDS-store phase): 1-4 % faster on every shape measured
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       h8 af[T::TM];
@@ -274,6 +277,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int b) {
     load(reg[u % PD], t + PD);
     __builtin_amdgcn_sched_barrier(0);  // issue the loads before the stage's MFMAs
     compute(u & 1, (u & 1) == 0);
+    __builtin_amdgcn_s_setprio(0);
     if (t + 1 < ns) store(reg[(u + 1) % PD], (u + 1) & 1, t + 1);
     __syncthreads();
   };
