@@ -362,6 +362,10 @@ def _single(rot, xd, w, dt):
     # batched transforms, then one decode launch per D over the transformed rows
     [(300 + i, (1, 3, 16, 5)[i % 4], 4224, 40 + 16 * i, 8) for i in range(6)]
     + [(310 + i, (2, 16)[i % 2], 512, 48, 12) for i in range(4)] + [(320, 4, 4224, 64, None)],
+    # GEMM-shaped calls of up to 256 rows with different tilings, rotated and plain: grouped
+    # launches (one per tiling and x order) and one grouped split reduction
+    [(500, 200, 1024, 2048, 8), (501, 20, 1024, 64, 8), (502, 250, 1024, 1536, None), (503, 17, 1024, 4096, None),
+     (504, 128, 2048, 256, 4), (505, 64, 4096, 1024, 8), (506, 64, 4096, 1024, None)],
     # one layer of the 1.5B-shaped stack at decode M = 1 (q, k, v, o, gate, up, down), as the
     # whole-stack decode step batches it
     [(400 + i, 1, s.D, s.N, s.K) for i, s in enumerate(W.MODEL_LINEARS)],
