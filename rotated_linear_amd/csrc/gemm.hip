@@ -31,7 +31,9 @@
 //     XCD is given a contiguous range of tile indices and tiles are numbered in column
 //     groups of kGroupM tile rows: an XCD's tiles share A rows and weight rows in its L2;
 //   * optional split-K: split s of S takes a contiguous range of groups and writes float32
-//     partial sums; a second kernel adds the S partials in order (deterministic).
+//     partial sums; a second kernel adds the S partials in order (deterministic);
+//   * independent calls with the same tiling can share one launch (a table of calls; each
+//     call's tiles are computed exactly as in its own launch), their reductions one more.
 #include <algorithm>
 #include <string.h>
 
