@@ -408,3 +408,32 @@ def test_batch_edge_cases():
     b = [C.host(y) for y in rl.paro_linear_batch(calls)]
     for u, v in zip(a, b):
         assert np.array_equal(u.view(np.uint16), v.view(np.uint16))
+
+
+@pytest.mark.parametrize("wid,Ms", [(2, (1, 4, 16)), (5, (64,))])
+def test_workload_batch_as_benchmarked(wid, Ms):
+    """The batched steps bench.py times, on the workload's own inputs: the attention projections
+    q, k, v, o at M = 1, 4, 16 in one call (decode launches with the transform inside), and the
+    8B-class layer's seven linears at M = 64 (batched transforms, grouped GEMM launches, one
+    grouped split reduction). Every output is bit-identical to its single call and meets the
+    spec bar against the oracle on sampled weight rows."""
+    C.log(f"workload {wid} batch at M={Ms}")
+    n_lin = {2: 4, 5: 7}[wid]
+    ins = []
+    for i in range(n_lin):
+        L = C.linear_inputs(wid, i)
+        rot = _rot(L)
+        w = rl.paro_pack_weights(rot, C.dev(L.W, torch))
+        for M in Ms:
+            ins.append((L, rot, C.dev(L.x[:M], torch), w))
+    calls = [(rot, xd, *w) for (L, rot, xd, w) in ins]
+    ys = [C.host(y) for y in rl.paro_linear_batch(calls, out_dtype=torch.float32)]
+    for (L, rot, xd, w), y in zip(ins, ys):
+        single = C.host(rl.paro_rotated_linear(rot, xd, *w, out_dtype=torch.float32))
+        assert np.array_equal(y.view(np.uint8), single.view(np.uint8)), (L.spec.name, xd.shape[0])
+        rows = C.sample_rows(L.spec.N, 256, seed=xd.shape[0])
+        deq = O.dequantize(*(C.host(t)[rows] for t in w))
+        a = O.transform_activations(L.x[:xd.shape[0]], L.pairs, L.theta, L.scale)
+        ref = O.f16_rne(a).astype(np.float64) @ deq.T
+        mx, rel = C.linear_metrics(y[:, rows], ref)
+        assert mx <= C.MAX_ABS and rel <= C.REL_L2, (L.spec.name, xd.shape[0], mx, rel)
