@@ -2,8 +2,8 @@
 // then division by the channel scales ("ParoQuant: pairwise rotations that
 // survive deployment", section "A rotation small enough to execute").
 //
-// One workgroup of NT threads (512; 1024 for a single row wider than 9216 channels,
-// which would otherwise leave each thread 12-14 pairs per stage) holds R rows in LDS as float32, interleaved by
+// One workgroup of NT threads (512; 1024 for a single row wider than 6144 channels,
+// which would otherwise leave each thread 9-14 pairs per stage) holds R rows in LDS as float32, interleaved by
 // channel (lds[c * R + r]: one R-wide vector per channel, so a stage moves a pair
 // of channels for all R rows with two vector reads and two vector writes), runs
 // the K stages (rotation_core.h) and writes fp16(rows * (1/s)). Workgroups are
@@ -228,11 +228,12 @@ hipError_t launch_ppt(const RotJobs& J, int grid, hipStream_t st) {
   if (P <= 1536) return launch_exact<512, R, 3, 4, PERM>(J, grid, st);
   if (P <= 2048) return launch_exact<512, R, 4, 4, PERM>(J, grid, st);
   if (P <= 3072) return launch_exact<512, R, 6, 2, PERM>(J, grid, st);
-  if (P <= 4608) return launch_exact<512, R, 9, 2, PERM>(J, grid, st);
   if constexpr (R == 1) {  // one wide row per workgroup (few rows): 1024 threads, half the pairs each
+    if (P <= 4608) return launch_exact<1024, R, 5, 2, PERM>(J, grid, st);
     if (P <= 6144) return launch_exact<1024, R, 6, 2, PERM>(J, grid, st);
     if (P <= 7168) return launch_exact<1024, R, 7, 2, PERM>(J, grid, st);
   }
+  if (P <= 4608) return launch_exact<512, R, 9, 2, PERM>(J, grid, st);
   if constexpr (R <= 2) {  // wider rows (D > 9216) never take 4 rows per workgroup
     // two stages of records in flight where the registers allow it (no spills): one stage
     // leaves every stage waiting for its records' round trip

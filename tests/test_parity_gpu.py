@@ -143,7 +143,7 @@ def test_rotate_identity_and_order():
 @pytest.mark.parametrize("M,D,K", [(1, 128, 0), (3, 128, 1), (5, 384, 3), (7, 16384, 2), (9, 1280, 8),
                                    (130, 640, 5),
                                    # one wide row per 1024-thread workgroup: exact (14336) and not
-                                   (100, 9344, 3), (33, 14336, 2), (40, 12544, 8),
+                                   (100, 9344, 3), (33, 14336, 2), (40, 12544, 8), (3, 8960, 8), (200, 6272, 4),
                                    # the most stages (rolled stage loop), one past the unrolled count
                                    (20, 1024, 64), (6, 2048, 9),
                                    # rows per block 2 and 4, widths at and past the 4-row limit
