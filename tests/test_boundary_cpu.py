@@ -275,3 +275,21 @@ def test_encode_errors_match_prepare():
     with pytest.raises(rl.ParoError) as e:
         rl.paro_rotation_encode(pairs, theta, s)
     assert e.value.status == 4
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """No CPU fallback: a copy of the package without libparo.so refuses to import."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "rotated_linear_amd")
+    dst = tmp_path / "rotated_linear_amd"
+    dst.mkdir()
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(pkg, f), dst / f)
+    r = subprocess.run([sys.executable, "-c", "import rotated_linear_amd"], cwd=tmp_path, capture_output=True,
+                       text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libparo.so is missing" in r.stderr
