@@ -223,8 +223,8 @@ hipError_t launch_exact(const RotJobs& J, int grid, hipStream_t st) {
 template <int R, bool PERM>
 hipError_t launch_ppt(const RotJobs& J, int grid, hipStream_t st) {
   const int P = J.D / 2;
-  if (P <= 512) return launch_exact<512, R, 1, 8, PERM>(J, grid, st);
-  if (P <= 1024) return launch_exact<512, R, 2, 8, PERM>(J, grid, st);
+  if (P <= 512) return launch_exact<512, R, 1, 4, PERM>(J, grid, st);
+  if (P <= 1024) return launch_exact<512, R, 2, 4, PERM>(J, grid, st);
   if (P <= 1536) return launch_exact<512, R, 3, 4, PERM>(J, grid, st);
   if (P <= 2048) return launch_exact<512, R, 4, 4, PERM>(J, grid, st);
   if (P <= 3072) return launch_exact<512, R, 6, 2, PERM>(J, grid, st);
