@@ -197,7 +197,9 @@ __global__ __launch_bounds__(NT) void rotate_rows_kernel(const RotJobs J) {
   }
 }
 
-// One launch over J (jobs of one D), `grid` workgroups.
+// One launch over J (jobs of one D): `grid` workgroups, or with grid = -T persistent workgroups
+// over T blocks, as many as the CUs hold at once (registers and LDS, from the runtime's occupancy
+// query: a workgroup that only starts when another ends would serve its blocks last).
 template <int NT, int R, int PPT, int PD, bool EXACT, bool PERM>
 hipError_t launch_rows(const RotJobs& J, int grid, hipStream_t st) {
   const size_t lds = size_t(J.D) * R * sizeof(float);
@@ -205,6 +207,11 @@ hipError_t launch_rows(const RotJobs& J, int grid, hipStream_t st) {
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
+  }
+  if (grid < 0) {
+    int per_cu = 0;
+    if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, lds)) return e;
+    grid = int(std::min<long>(-long(grid), long(std::max(per_cu, 1)) * kCUs));
   }
   hipLaunchKernelGGL((rotate_rows_kernel<NT, R, PPT, PD, EXACT, PERM>), dim3(grid), dim3(NT), lds, st, J);
   return hipGetLastError();
@@ -225,9 +232,9 @@ hipError_t launch_ppt(const RotJobs& J, int grid, hipStream_t st) {
   const int P = J.D / 2;
   if (P <= 512) return launch_exact<512, R, 1, 4, PERM>(J, grid, st);
   if (P <= 1024) return launch_exact<512, R, 2, 4, PERM>(J, grid, st);
-  if (P <= 1536) return launch_exact<512, R, 3, 4, PERM>(J, grid, st);
-  if (P <= 2048) return launch_exact<512, R, 4, 4, PERM>(J, grid, st);
-  if (P <= 3072) return launch_exact<512, R, 6, 2, PERM>(J, grid, st);
+  if (P <= 1536) return launch_exact<512, R, 3, (R == 4 ? 2 : 4), PERM>(J, grid, st);
+  if (P <= 2048) return launch_exact<512, R, 4, (R == 1 ? 4 : 2), PERM>(J, grid, st);
+  if (P <= 3072) return launch_exact<512, R, 6, (R == 2 ? 1 : 2), PERM>(J, grid, st);
   if constexpr (R == 1) {  // one wide row per workgroup (few rows): 1024 threads, half the pairs each
     if (P <= 4608) return launch_exact<1024, R, 5, 2, PERM>(J, grid, st);
     if (P <= 6144) return launch_exact<1024, R, 6, 2, PERM>(J, grid, st);
@@ -276,8 +283,7 @@ hipError_t launch_jobs(const RotateJob* jobs, int n, int R, bool perm, hipStream
     total += (jobs[i].M + R - 1) / R;
   }
   J.blk0[n] = total;
-  const long per_cu = std::max<long>(1, long(kRotLds / (size_t(J.D) * R * sizeof(float))));
-  const int grid = n == 1 ? int(std::min<long>(total, per_cu * kCUs)) : total;
+  const int grid = n == 1 ? -total : total;  // one job: persistent workgroups (see launch_rows)
   if (R == 4) return perm ? launch_ppt<4, true>(J, grid, st) : launch_ppt<4, false>(J, grid, st);
   if (R == 2) return perm ? launch_ppt<2, true>(J, grid, st) : launch_ppt<2, false>(J, grid, st);
   return perm ? launch_ppt<1, true>(J, grid, st) : launch_ppt<1, false>(J, grid, st);
