@@ -157,7 +157,29 @@ def capture(torch, fn, n_graphs):
     return graphs
 
 
-def time_graphs(torch, graphs, steps, warmup, min_warm_s=0.0):
+def read_sclk_mhz():
+    """The shader clock the driver reports for the first GPU right now (the starred level of
+    sysfs pp_dpm_sclk) and the highest level it lists, in MHz; None where sysfs does not say."""
+    import glob
+    import re
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                lines = f.read().splitlines()
+        except OSError:
+            continue
+        levels = [(int(m.group(1)), ln.rstrip().endswith("*"))
+                  for ln in lines for m in [re.search(r"(\d+)\s*mhz", ln, re.I)] if m]
+        if levels:
+            cur = [v for v, star in levels if star]
+            return {"now": cur[0] if cur else None, "max_level": max(v for v, _ in levels)}
+    return None
+
+
+SCLK_SAMPLES = []  # (label, read_sclk_mhz()) taken while timed GPU work runs
+
+
+def time_graphs(torch, graphs, steps, warmup, min_warm_s=0.0, sclk_label=None):
     """Replay graphs[t % len] for t < steps; returns ms per step (events bracket the K steps).
     Before them: `warmup` untimed replays, continued until at least `min_warm_s` seconds have
     passed (an idle GPU lowers its clocks; a few ms of work bring them back)."""
@@ -175,18 +197,20 @@ def time_graphs(torch, graphs, steps, warmup, min_warm_s=0.0):
     for t in range(steps):
         graphs[t % len(graphs)].replay()
     end.record()
+    if sclk_label is not None:  # the replays are still running: read the clock under load
+        SCLK_SAMPLES.append((sclk_label, read_sclk_mhz()))
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
 
 
-def time_slots(torch, fn, n_slots, per, steps, warmup, min_warm_s=0.05):
+def time_slots(torch, fn, n_slots, per, steps, warmup, min_warm_s=0.05, sclk_label=None):
     """fn(slot) for slot < n_slots, captured as graphs of `per` consecutive slots (so one replay
     carries several steps and host launch cost stays out of the per-step time); returns ms per
     step over `steps` steps after `warmup` untimed ones (and at least `min_warm_s` seconds of
     them)."""
     n_graphs = max(1, n_slots // per)
     gs = capture(torch, lambda g: [fn(g * per + r) for r in range(per)], n_graphs)
-    ms = time_graphs(torch, gs, max(1, steps // per), max(1, warmup // per), min_warm_s) / per
+    ms = time_graphs(torch, gs, max(1, steps // per), max(1, warmup // per), min_warm_s, sclk_label) / per
     del gs
     return ms
 
@@ -261,6 +285,9 @@ def attainable(torch):
     for _ in range(10):
         torch.matmul(x, w)
     e1.record()
+    for i in range(4):  # the 10 products take about 10 ms: four samples 2 ms apart
+        SCLK_SAMPLES.append(("vendor fp16 GEMM #%d" % i, read_sclk_mhz()))
+        time.sleep(0.002)
     torch.cuda.synchronize()
     out["fp16_gemm_TFLOPs"] = round(2.0 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
     del x, w
@@ -315,7 +342,8 @@ def main():
 
     def timed(rotated, batched):  # exactly --warmup untimed steps, then --steps timed ones
         return time_slots(torch, lambda s: step.enqueue(s, rotated=rotated, batched=batched), n_graphs * per_graph,
-                          per_graph, args.steps, args.warmup, min_warm_s=0.0)
+                          per_graph, args.steps, args.warmup, min_warm_s=0.0,
+                          sclk_label="attention decode step" if rotated and batched else None)
 
     # the step: the 12 projections as one batched call (one launch of the decode kernel)
     ms_rot = timed(True, True)
@@ -346,6 +374,7 @@ def main():
                    "algorithmic_bytes_per_step": bytes_rot, "cold_pool_bytes": pool_bytes},
         "roofline": roofline,
         "attainable": att,
+        "sclk_mhz_under_load": {label: v for label, v in SCLK_SAMPLES},
         "rotation_overhead_pct": round(overhead, 2),
         "plain_w4a16": {"ms_per_step": round(ms_plain, 6),
                         "GB/s": round(step.bytes(False) / (ms_plain * 1e-3) / 1e9, 3)},
