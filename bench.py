@@ -1,21 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the rotated W4A16 linear on one MI355X.
 
-Workload (default): the Qwen2.5-1.5B-shaped attention projections in decode --
-q, k, v, o (D=1536 -> N=1536/256/256/1536), K=8 Givens stages, INT4 group 128 --
-at M = 1, 4 and 16 tokens. One step = the 12 rotated linears (4 linears x 3
-batch sizes) as one paro_linear_batch call, i.e. one launch of the decode kernel
-with each transform run inside it. Every call reads its weights, scales, zeros
-and transform descriptor cold from HBM: each step takes the next copies from a
-pool larger than 1 GiB (four times the 256 MB Infinity Cache). Steps are
-replayed as HIP graphs captured from the library's own launches, so Python call
-overhead stays out of the timed region. The same 12 calls made one library call
-each are reported beside it.
+Headline workload: the seven linears of one 8B-class decoder layer (q, k, v, o:
+4096 -> 4096/1024/1024/4096; gate, up: 4096 -> 14336; down: 14336 -> 4096), each
+with its own transform of K = 8 Givens stages and channel scaling, INT4 group 128.
+One decode step = the seven rotated linears at M = 64 tokens as one
+paro_linear_batch call. Every step reads its weights, scales, zeros and transform
+descriptors cold from HBM: each step takes the next copies from a pool larger than
+1 GiB (four times the 256 MB Infinity Cache). Steps are replayed as HIP graphs
+captured from the library's own launches, so Python call overhead stays out of
+the timed region, and the timed replays continue the pool rotation where the
+warm-up replays stopped.
 
 Prints ONE JSON line: decode HBM GB/s of the whole step (algorithmic bytes /
-time), the roofline of the dominant kernel, the CPU oracle's throughput on a
-bounded sample, the rotation overhead against the plain INT4 linear on the same
-step, and prefill / large-decode extras (gate+up decode, down_proj prefill).
+time) with the roofline of its linear kernel, the prefill step of the same layer
+(M = 4096) in TFLOP/s with its own roofline, the rotation overhead of both
+against the plain INT4 linear on the same packed weights, the CPU oracle's
+throughput on bounded samples of each workload, and extras (the Qwen2.5-1.5B-
+shaped attention decode step, gate+up decode and prefill, down_proj prefill,
+overhead against the stage count, the whole-stack decode and build, chunked
+prefill overlap).
 """
 from __future__ import annotations
 
@@ -38,17 +42,18 @@ POOL_BYTES = int(1.1 * (1 << 30))
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=1000)  # about 14 ms: the GPU clocks settle
-    p.add_argument("--no-extras", action="store_true", help="skip the gate+up / down_proj extras")
-    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--traffic", action="store_true",
-                   help="for rocprofv3 --pmc runs: a 256 MiB float16 negation (the counter calibration copy) "
-                        "and then the dominant call over the cold pool, eagerly; prints nothing else")
-    p.add_argument("--prefill-only", action="store_true",
-                   help="for rocprofv3 runs: only the down_proj prefill (M=2048, D=8960, N=1536), --steps rotated "
-                        "then --steps plain calls, eagerly; prints one line of event timings")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-extras", action="store_true", help="skip the extras")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time of the headline's oracle sample")
+    p.add_argument("--only", choices=("decode", "prefill"),
+                   help="for rocprofv3 runs: only the 8B-class layer's decode (M=64) or prefill (M=4096) step, "
+                        "rotated then plain, timed as in the full run; prints one JSON line")
+    p.add_argument("--traffic", choices=("decode", "prefill"),
+                   help="for rocprofv3 --pmc runs: a 256 MiB float16 negation (the counter calibration copy), "
+                        "then --steps plain linear steps of the 8B-class layer (the step's linear kernel alone), "
+                        "eagerly, each on its own pool copy; prints one JSON line")
     return p.parse_args()
 
 
@@ -180,9 +185,11 @@ SCLK_SAMPLES = []  # (label, read_sclk_mhz()) taken while timed GPU work runs
 
 
 def time_graphs(torch, graphs, steps, warmup, min_warm_s=0.0, sclk_label=None):
-    """Replay graphs[t % len] for t < steps; returns ms per step (events bracket the K steps).
-    Before them: `warmup` untimed replays, continued until at least `min_warm_s` seconds have
-    passed (an idle GPU lowers its clocks; a few ms of work bring them back)."""
+    """Replay graphs round-robin: `warmup` untimed replays (continued until at least `min_warm_s`
+    seconds have passed: an idle GPU lowers its clocks, a few ms of work bring them back), then
+    `steps` timed ones bracketed by HIP events on the replay stream. The timed replays continue the
+    rotation where the warm-up stopped, so the first timed graph is not one the warm-up has just
+    run (its copies could still sit in the Infinity Cache). Returns ms per replay."""
     t0 = time.perf_counter()
     t = 0
     while t < warmup or time.perf_counter() - t0 < min_warm_s:
@@ -194,8 +201,8 @@ def time_graphs(torch, graphs, steps, warmup, min_warm_s=0.0, sclk_label=None):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for t in range(steps):
-        graphs[t % len(graphs)].replay()
+    for u in range(steps):
+        graphs[(t + u) % len(graphs)].replay()
     end.record()
     if sclk_label is not None:  # the replays are still running: read the clock under load
         SCLK_SAMPLES.append((sclk_label, read_sclk_mhz()))
@@ -206,22 +213,35 @@ def time_graphs(torch, graphs, steps, warmup, min_warm_s=0.0, sclk_label=None):
 def time_slots(torch, fn, n_slots, per, steps, warmup, min_warm_s=0.05, sclk_label=None):
     """fn(slot) for slot < n_slots, captured as graphs of `per` consecutive slots (so one replay
     carries several steps and host launch cost stays out of the per-step time); returns ms per
-    step over `steps` steps after `warmup` untimed ones (and at least `min_warm_s` seconds of
-    them)."""
+    step over `steps` steps (rounded up to whole graphs) after `warmup` untimed ones (and at least
+    `min_warm_s` seconds of them)."""
     n_graphs = max(1, n_slots // per)
     gs = capture(torch, lambda g: [fn(g * per + r) for r in range(per)], n_graphs)
-    ms = time_graphs(torch, gs, max(1, steps // per), max(1, warmup // per), min_warm_s, sclk_label) / per
+    ms = time_graphs(torch, gs, max(1, -(-steps // per)), -(-warmup // per), min_warm_s, sclk_label) / per
     del gs
     return ms
 
 
 # --------------------------------------------------------------------------- #
-# CPU oracle baseline
+# CPU oracle baselines
 # --------------------------------------------------------------------------- #
 
-def cpu_baseline(step, seconds):
-    """The oracle's per-call path (float64 transform + x' . deq^T, deq precomputed) on the same
-    calls as a GPU step, repeated for about ``seconds`` of wall time."""
+def _blas_threads():
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+                                 if i.get("user_api") == "blas"})) or "unknown"
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores, blas = os.cpu_count() or 1, "unknown"
+    return int(cores), blas
+
+
+def cpu_baseline(step, seconds, rows=None):
+    """The oracle's per-call path (float64 transform + x' . deq^T, deq precomputed) on the calls of
+    a GPU step, repeated for about ``seconds`` of wall time. ``rows``: compute only that many
+    output columns of each call (the weight rows are independent), counting bytes for those."""
     import numpy as np
 
     import oracle as O
@@ -229,7 +249,8 @@ def cpu_baseline(step, seconds):
     deq = {}
     for li, lin in enumerate(step.linears):
         qw, sc, z = (t.cpu().numpy() for t in lin.w)
-        deq[li] = O.dequantize(qw, sc, z)
+        n = lin.N if rows is None else min(rows, lin.N)
+        deq[li] = O.dequantize(qw[:n], sc[:n], z[:n])
     xs = {k: v.cpu().numpy() for k, v in step.x.items()}
     n_steps, t0 = 0, time.perf_counter()
     while True:
@@ -241,19 +262,34 @@ def cpu_baseline(step, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    blas = "unknown"
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] or [1])
-        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info if i.get("user_api") == "blas"})) or blas
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        cores = os.cpu_count() or 1
-    gbs = step.bytes() * n_steps / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_steps} oracle passes over the step's {len(step.calls)} calls "
-                      f"(float64 transform + x'.deq^T, deq precomputed) in {el:.1f} s; "
+    cores, blas = _blas_threads()
+    nbytes = sum(workload_bytes(M, step.linears[li].D, deq[li].shape[0], step.linears[li].K) for li, M in step.calls)
+    gbs = nbytes * n_steps / el / 1e9
+    cols = "" if rows is None else f", the first {rows} output columns of each"
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_steps} oracle passes over the step's {len(step.calls)} calls{cols} "
+                      f"(float64 transform + x'.deq^T, deq precomputed) in {el:.1f} s, single pass each; "
                       f"host {os.cpu_count()} logical CPUs, BLAS threads {cores} ({blas})"}
+
+
+def cpu_pack_baseline(lins, rows, seconds):
+    """The oracle's build-time path (float64 fold, quantize, pack) on the first ``rows`` weight rows
+    of each linear, repeated for about ``seconds``; weights per second."""
+    import oracle as O
+
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for lin in lins:
+            L = lin.L
+            O.pack_weights(L.W[:rows], L.pairs, L.theta, L.scale)
+            n += rows * lin.D
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    cores, blas = _blas_threads()
+    return {"value": round(n / el / 1e6, 3), "unit": "Mweights/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 fold + quantize + pack of {rows} weight rows of each of {len(lins)} linears, "
+                      f"{n} weights in {el:.1f} s"}
 
 
 def attainable(torch):
@@ -330,60 +366,36 @@ def main():
 
     torch.cuda.init()
     if args.traffic:
-        traffic_run(rl, torch, W, args.steps)
+        traffic_run(rl, torch, W, args.traffic, args.steps)
         return
-    if args.prefill_only:
-        prefill_run(rl, torch, W, args.steps)
+    layer = Layer8B(rl, torch, W)
+    if args.only:
+        res = layer.decode(args) if args.only == "decode" else layer.prefill(args)
+        print(json.dumps({"only": args.only, **res}), flush=True)
         return
-    step, pool_bytes = attention_step(rl, torch, W)
-    n_slots = step.n_slots
-    per_graph = math.gcd(args.steps, 8) or 1  # steps per captured graph (divides K exactly)
-    n_graphs = max(1, n_slots // per_graph)
 
-    def timed(rotated, batched):  # exactly --warmup untimed steps, then --steps timed ones
-        return time_slots(torch, lambda s: step.enqueue(s, rotated=rotated, batched=batched), n_graphs * per_graph,
-                          per_graph, args.steps, args.warmup, min_warm_s=0.0,
-                          sclk_label="attention decode step" if rotated and batched else None)
-
-    # the step: the 12 projections as one batched call (one launch of the decode kernel)
-    ms_rot = timed(True, True)
-    ms_plain = timed(False, True)
-    bytes_rot = step.bytes(True)
-    value = bytes_rot / (ms_rot * 1e-3) / 1e9
-    overhead = (ms_rot - ms_plain) / ms_plain * 100.0
-    # the same calls one library call each (12 launches)
-    ms_calls_rot = timed(True, False)
-    ms_calls_plain = timed(False, False)
-
-    # dominant kernel: the step's single decode launch; its average duration is the step time
-    # measured above (HIP events on the replay stream around whole graphs of launches)
+    dec = layer.decode(args, sclk_label="8B-class layer decode step")
+    pre = layer.prefill(args)
     att = attainable(torch)
-    roofline = {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "kernel": "decode_kernel<2,3,4> (12 rotated projections, transform inside)",
-                "avg_launch_us": round(ms_rot * 1e3, 3), "algorithmic_bytes_per_launch": bytes_rot,
-                "frac_of_attainable": round(value / att["hbm_copy_GBps"], 4)}
-
+    for r in (dec["roofline"], pre["roofline"]):
+        base = att["hbm_copy_GBps"] if r["unit"] == "GB/s" else att["fp16_gemm_TFLOPs"]
+        r["frac_of_attainable"] = round(r["achieved"] / base, 4)
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_rot, 6), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": dec["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "Qwen2.5-1.5B attention projections q,k,v,o decode (D=1536; N=1536,256,256,1536)",
-                   "M": list(step.Ms), "K_stages": 8, "group": 128, "calls_per_step": len(step.calls),
-                   "launch": "one paro_linear_batch call per step, HIP graphs of %d steps" % per_graph,
-                   "algorithmic_bytes_per_step": bytes_rot, "cold_pool_bytes": pool_bytes},
-        "roofline": roofline,
+        "config": {"workload": "8B-class decoder layer, decode: q, k, v, o, gate, up, down "
+                               "(4096->4096/1024/1024/4096/14336/14336, 14336->4096), each with its own transform",
+                   "M": 64, "K_stages": 8, "group": 128, "calls_per_step": 7,
+                   "launch": dec["launch"], "algorithmic_bytes_per_step": dec["algorithmic_bytes"],
+                   "cold_pool_bytes": dec["cold_pool_bytes"]},
+        "roofline": dec["roofline"],
+        "rotation_overhead_pct": dec["overhead_pct"],
+        "plain_w4a16": dec["plain"],
+        "prefill": {k: v for k, v in pre.items() if k != "roofline"},
+        "roofline_prefill": pre["roofline"],
         "attainable": att,
-        "sclk_mhz_under_load": {label: v for label, v in SCLK_SAMPLES},
-        "rotation_overhead_pct": round(overhead, 2),
-        "plain_w4a16": {"ms_per_step": round(ms_plain, 6),
-                        "GB/s": round(step.bytes(False) / (ms_plain * 1e-3) / 1e9, 3)},
-        "separate_calls": {"ms_per_step": round(ms_calls_rot, 6),
-                           "GB/s": round(bytes_rot / (ms_calls_rot * 1e-3) / 1e9, 3),
-                           "plain_ms_per_step": round(ms_calls_plain, 6),
-                           "rotation_overhead_pct": round((ms_calls_rot - ms_calls_plain) / ms_calls_plain * 100, 2)},
     }
-
     if not args.no_extras:
         out["extras"] = extras(rl, torch, W, args)
         for e in out["extras"].values():  # the same results against what the box attains
@@ -391,37 +403,42 @@ def main():
                 e["frac_of_attainable_gemm"] = round(e["TFLOP/s"] / att["fp16_gemm_TFLOPs"], 4)
             if "GB/s" in e:
                 e["frac_of_attainable_hbm"] = round(e["GB/s"] / att["hbm_copy_GBps"], 4)
+    out["sclk_mhz_under_load"] = {label: v for label, v in SCLK_SAMPLES}
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(layer.decode_step, args.cpu_seconds, rows=2048)
+        out["cpu_baseline_by_workload"] = cpu_by_workload(rl, torch, W, layer)
     print(json.dumps(out), flush=True)
 
 
 CALIB_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_step_traffic.md")
-KERNEL_SOURCES = ["rotated_linear_amd/csrc/decode.hip", "rotated_linear_amd/csrc/rotation_core.h",
-                  "rotated_linear_amd/csrc/paro_internal.h"]
+# counter summaries of the headline steps' linear kernel, each valid only for the kernel sources it
+# was taken on
+TRAFFIC_FILES = {"decode": os.path.join(ROOT, "profiles", "traffic_layer8b_decode_M64.md"),
+                 "prefill": os.path.join(ROOT, "profiles", "traffic_layer8b_prefill_M4096.md")}
+KERNEL_SOURCES = {"decode": ["rotated_linear_amd/csrc/gemm.hip", "rotated_linear_amd/csrc/paro_internal.h"],
+                  "prefill": ["rotated_linear_amd/csrc/gemm.hip", "rotated_linear_amd/csrc/paro_internal.h"]}
 
 
-def kernel_source_hash():
+def kernel_source_hash(which):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[which]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
+def measured_traffic(which):
+    """HBM bytes per launch of the step's linear kernel from the committed counter summary, or None
     when that summary was taken on other kernel sources than the ones built here."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC_FILES[which]) as fh:
             for line in fh:
                 if " = " in line:
                     k, v = line.split(" = ", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("source_sha256_16") != kernel_source_hash():
+        if kv.get("source_sha256_16") != kernel_source_hash(which):
             return None
         return int(float(kv["traffic_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
@@ -443,44 +460,124 @@ def attention_step(rl, torch, W):
     return step, set_bytes * n_sets
 
 
-def traffic_run(rl, torch, W, reps):
+def traffic_run(rl, torch, W, which, reps):
+    """Calibration copy, then `reps` plain linear steps of the 8B-class layer (decode M = 64 or
+    prefill M = 4096), eagerly, each on its own pool copy (cold reads)."""
     a = torch.ones(CALIB_BYTES // 2, dtype=torch.float16, device="cuda")
     b = torch.empty_like(a)
     for _ in range(3):
         torch.neg(a, out=b)
     torch.cuda.synchronize()
     del a, b
-    st, _ = attention_step(rl, torch, W)
+    layer = Layer8B(rl, torch, W)
+    st = layer.decode_step if which == "decode" else layer.prefill_step()
     for r in range(reps):
-        st.enqueue(r, rotated=True, batched=True)
+        st.enqueue(r, rotated=False, batched=True)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_run": {"steps": reps, "calib_bytes": CALIB_BYTES}}), flush=True)
+    print(json.dumps({"traffic_run": {"step": which, "steps": reps, "calib_bytes": CALIB_BYTES}}), flush=True)
 
 
-def prefill_run(rl, torch, W, reps):
-    """The down_proj prefill alone (rotated, then plain), for kernel traces and counters."""
-    L4 = Linear(rl, torch, W.make_linear(4, 0))
-    st = Step(rl, torch, [L4], [2048])
-    out = {}
-    for rotated in (True, False):
-        for _ in range(3):
-            st.enqueue(0, rotated=rotated)
+def _divisor_at_most(k, cap):
+    """The largest divisor of k that is at most cap (>= 1)."""
+    for p in range(max(1, min(cap, k)), 0, -1):
+        if k % p == 0:
+            return p
+    return 1
+
+
+class Layer8B:
+    """The 8B-class decoder layer's seven linears (q, k, v, o, gate, up, down), each with its own
+    transform, packed once on the GPU, with a pool of copies (weights, scales, zeros and
+    descriptors) larger than 1 GiB so that every step reads cold from HBM."""
+
+    DECODE_M, PREFILL_M = 64, 4096
+
+    def __init__(self, rl, torch, W):
+        self.rl, self.torch = rl, torch
+        self.lins = [Linear(rl, torch, W.make_linear(5, i)) for i in range(len(W.WORKLOADS[5].linears))]
+        self.set_bytes = sum(l.set_bytes() for l in self.lins)
+        self.n_sets = max(4, math.ceil(POOL_BYTES / self.set_bytes))
+        for l in self.lins:
+            l.make_copies(rl, self.n_sets)
+        self.decode_step = Step(rl, torch, self.lins, [self.DECODE_M])
+        self._prefill = None
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            st.enqueue(0, rotated=rotated)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        out["rotated" if rotated else "plain"] = {"us": round(us, 2), "TFLOP/s": round(st.flops() / us / 1e6, 2)}
-    print(json.dumps({"prefill_only": "down_proj M=2048 D=8960 N=1536 K=8", **out}), flush=True)
+
+    def prefill_step(self):
+        if self._prefill is None:
+            self._prefill = Step(self.rl, self.torch, self.lins, [self.PREFILL_M])
+        return self._prefill
+
+    def _time(self, st, rotated, steps, warmup, per, sclk_label=None):
+        n_graphs = max(2, self.n_sets // per)
+        return time_slots(self.torch, lambda s: st.enqueue(s, rotated=rotated, batched=True), n_graphs * per, per,
+                          steps, warmup, min_warm_s=0.0, sclk_label=sclk_label)
+
+    def decode(self, args, sclk_label=None):
+        """The decode step: the seven rotated linears at M = 64 as one paro_linear_batch call, timed
+        over exactly --steps steps after --warmup untimed ones; beside it the plain linears on the
+        same packed weights (the step's linear kernel alone)."""
+        st = self.decode_step
+        per = _divisor_at_most(args.steps, min(8, self.n_sets // 2))
+        ms_rot = self._time(st, True, args.steps, args.warmup, per, sclk_label)
+        ms_plain = self._time(st, False, args.steps, args.warmup, per)
+        bytes_rot, bytes_plain = st.bytes(True), st.bytes(False)
+        gbs = bytes_rot / (ms_rot * 1e-3) / 1e9
+        lin_gbs = bytes_plain / (ms_plain * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(lin_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(lin_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
+                    "kernel": "the step's INT4 linear launch (paro_linear_batch of the seven plain linears "
+                              "on the same packed weights; event-timed graph replays of that launch alone)",
+                    "avg_launch_us": round(ms_plain * 1e3, 3), "algorithmic_bytes_per_launch": bytes_plain}
+        return {"GB/s": round(gbs, 3), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "ms_per_step": round(ms_rot, 6),
+                "us": round(ms_rot * 1e3, 3), "algorithmic_bytes": bytes_rot,
+                "overhead_pct": round((ms_rot - ms_plain) / ms_plain * 100.0, 2),
+                "plain": {"us": round(ms_plain * 1e3, 3), "GB/s": round(lin_gbs, 3)},
+                "launch": "one paro_linear_batch call per step, HIP graphs of %d steps" % per,
+                "cold_pool_bytes": self.set_bytes * self.n_sets, "roofline": roofline}
+
+    def prefill(self, args):
+        """The prefill step: the seven rotated linears at M = 4096 as one paro_linear_batch call
+        (weights from the cold pool), and the plain linears beside it."""
+        st = self.prefill_step()
+        steps = max(4, args.steps // 2)
+        per = _divisor_at_most(steps, min(4, self.n_sets // 2))
+        ms_rot = self._time(st, True, steps, max(2, args.warmup // 2), per)
+        ms_plain = self._time(st, False, steps, max(2, args.warmup // 2), per)
+        fl = st.flops()
+        tf = fl / (ms_rot * 1e-3) / 1e12
+        lin_tf = fl / (ms_plain * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(lin_tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(lin_tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": measured_traffic("prefill"),
+                    "kernel": "the step's INT4 GEMM launches (paro_linear_batch of the seven plain linears "
+                              "on the same packed weights)",
+                    "avg_launch_us": round(ms_plain * 1e3, 3), "algorithmic_flop_per_launch": fl}
+        return {"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "M": self.PREFILL_M,
+                "steps": steps, "us": round(ms_rot * 1e3, 2), "flop": fl,
+                "overhead_pct": round((ms_rot - ms_plain) / ms_plain * 100.0, 2),
+                "plain": {"us": round(ms_plain * 1e3, 2), "TFLOP/s": round(lin_tf, 2)}, "roofline": roofline}
+
+
+def cpu_by_workload(rl, torch, W, layer):
+    """The oracle's per-call path on bounded samples of the other workloads, and its build-time
+    path (fold, quantize, pack) on the 8B-class layer's weights."""
+    res = {}
+    att = [Linear(rl, torch, W.make_linear(2, i)) for i in range(4)]
+    res["attention_decode_step_M1_4_16"] = cpu_baseline(Step(rl, torch, att, [1, 4, 16]), 3.0)
+    gu = Linear(rl, torch, W.make_linear(3, 0))
+    res["gate_up_M1_16_256"] = cpu_baseline(Step(rl, torch, [gu], [1, 16, 256]), 3.0, rows=2048)
+    dn = Linear(rl, torch, W.make_linear(4, 0))
+    res["down_prefill_M2048"] = cpu_baseline(Step(rl, torch, [dn], [2048]), 3.0, rows=256)
+    res["pack_layer8b"] = cpu_pack_baseline(layer.lins, 32, 4.0)
+    return res
 
 
 def extras(rl, torch, W, args):
-    """Larger shapes, rotated vs plain: gate+up decode (HBM) and prefill at M = 256 (MFMA), down_proj
-    prefill (MFMA), and the 8B-class layer at decode M = 64 and prefill M = 4096."""
+    """The Qwen2.5-1.5B-shaped workloads, rotated vs plain: the attention projections' decode step,
+    gate+up decode (HBM) and prefill at M = 256 (MFMA), down_proj prefill (MFMA); the overhead
+    against the stage count; the whole-stack decode and build; chunked prefill overlap."""
     res = {}
+    res.update(attention_decode(rl, torch, W, args))
     L3 = Linear(rl, torch, W.make_linear(3, 0))
     n3 = max(4, math.ceil(POOL_BYTES / L3.set_bytes()))
     L3.make_copies(rl, n3)
@@ -490,12 +587,11 @@ def extras(rl, torch, W, args):
         ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), n3, 8, 2 * n3, 16)
         res[f"gate_up_decode_M{M}"] = {"GB/s": round(st.bytes() / (ms_r * 1e-3) / 1e9, 2),
                                        "frac_hbm": round(st.bytes() / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                       "us": round(ms_r * 1e3, 3),
+                                       "us": round(ms_r * 1e3, 3), "plain_us": round(ms_p * 1e3, 3),
                                        "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
-    L3.copies = []
-    st = Step(rl, torch, [L3], [256])  # gate+up at M = 256: MFMA-bound
-    ms_r = time_slots(torch, lambda s: st.enqueue(s), 4, 4, 20, 4)
-    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), 4, 4, 20, 4)
+    st = Step(rl, torch, [L3], [256])  # gate+up at M = 256: MFMA-bound (weights from the cold pool)
+    ms_r = time_slots(torch, lambda s: st.enqueue(s), n3, 4, 20, 4)
+    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), n3, 4, 20, 4)
     tf = st.flops() / (ms_r * 1e-3) / 1e12
     res["gate_up_prefill_M256"] = {"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                    "us": round(ms_r * 1e3, 2),
@@ -503,20 +599,43 @@ def extras(rl, torch, W, args):
                                    "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
     del st, L3
     L4 = Linear(rl, torch, W.make_linear(4, 0))
+    n4 = max(4, math.ceil(POOL_BYTES / 2 / L4.set_bytes()))
+    L4.make_copies(rl, n4)
     st = Step(rl, torch, [L4], [2048])
-    ms_r = time_slots(torch, lambda s: st.enqueue(s), 4, 4, 20, 4)
-    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), 4, 4, 20, 4)
+    ms_r = time_slots(torch, lambda s: st.enqueue(s), n4, 4, 20, 4)
+    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False), n4, 4, 20, 4)
     tf = st.flops() / (ms_r * 1e-3) / 1e12
     res["down_prefill_M2048"] = {"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                  "us": round(ms_r * 1e3, 2),
                                  "plain_TFLOP/s": round(st.flops() / (ms_p * 1e-3) / 1e12, 2),
                                  "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
     del st, L4
-    res.update(layer8b(rl, torch, W, args))
     res.update(overhead_vs_k(rl, torch, W, args))
     res.update(model_stack(rl, torch, W, args))
     res.update(prefill_overlap(rl, torch, W, args))
     return res
+
+
+def attention_decode(rl, torch, W, args):
+    """The Qwen2.5-1.5B-shaped attention projections q, k, v, o (D = 1536) at M = 1, 4, 16: the 12
+    rotated calls as one paro_linear_batch call per step, and as 12 library calls, over a cold pool."""
+    step, pool_bytes = attention_step(rl, torch, W)
+    per = 8
+    n = max(1, step.n_slots // per) * per
+
+    def timed(rotated, batched):
+        return time_slots(torch, lambda s: step.enqueue(s, rotated=rotated, batched=batched), n, per, 200, 200,
+                          min_warm_s=0.05)
+    ms_rot, ms_plain = timed(True, True), timed(False, True)
+    ms_calls_rot, ms_calls_plain = timed(True, False), timed(False, False)
+    b = step.bytes(True)
+    return {"attention_decode_step": {
+        "GB/s": round(b / (ms_rot * 1e-3) / 1e9, 2), "frac_hbm": round(b / (ms_rot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "us": round(ms_rot * 1e3, 3), "algorithmic_bytes": b, "plain_us": round(ms_plain * 1e3, 3),
+        "overhead_pct": round((ms_rot - ms_plain) / ms_plain * 100, 2), "cold_pool_bytes": pool_bytes,
+        "separate_calls": {"us": round(ms_calls_rot * 1e3, 3), "plain_us": round(ms_calls_plain * 1e3, 3),
+                           "overhead_pct": round((ms_calls_rot - ms_calls_plain) / ms_calls_plain * 100, 2)},
+        "launch": "one paro_linear_batch call of the 12 projections per step"}}
 
 
 def prefill_overlap(rl, torch, W, args):
@@ -680,7 +799,10 @@ def model_stack(rl, torch, W, args):
         for c, o in zip(phases[rotated], ys_ph):
             rl.paro_linear_batch(c, outs=o)
 
-    for name, fn in (("grouped", run_grouped), ("layered", run_layered)):
+    # The layered order is the decode step a model makes (each layer's linears wait for the
+    # previous phase); the grouped one treats all 196 linears as independent calls, which no
+    # real decode step can do: it bounds what batching the launches would give.
+    for name, fn in (("layered", run_layered), ("grouped", run_grouped)):
         ms_r = time_slots(torch, lambda s: fn(True), 2, 1, 10, 2)
         ms_p = time_slots(torch, lambda s: fn(False), 2, 1, 10, 2)
         gbs = bytes_r / (ms_r * 1e-3) / 1e9
@@ -689,38 +811,11 @@ def model_stack(rl, torch, W, args):
             "algorithmic_bytes": bytes_r, "plain_us": round(ms_p * 1e3, 2),
             "plain_GB/s": round(bytes_p / (ms_p * 1e-3) / 1e9, 2),
             "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2),
-            "launch": "one paro_linear_batch call for all 196 linears" if name == "grouped" else
-                      "4 paro_linear_batch calls per layer (q/k/v, o, gate/up, down), 112 per step"}
-    return res
-
-
-def layer8b(rl, torch, W, args):
-    """The 8B-class decoder layer (7 linears, each with its own transform): decode at M = 64 as one
-    batched call over a cold pool (HBM-bound), and prefill at M = 4096 (MFMA-bound)."""
-    res = {}
-    lins = [Linear(rl, torch, W.make_linear(5, i)) for i in range(len(W.WORKLOADS[5].linears))]
-    set_bytes = sum(l.set_bytes() for l in lins)
-    n_sets = max(2, math.ceil(0.6 * POOL_BYTES / set_bytes))  # about 2.5 times the Infinity Cache
-    for l in lins:
-        l.make_copies(rl, n_sets)
-    st = Step(rl, torch, lins, [64])
-    ms_r = time_slots(torch, lambda s: st.enqueue(s, batched=True), n_sets, 2, 4 * n_sets, n_sets)
-    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False, batched=True), n_sets, 2, 4 * n_sets, n_sets)
-    gbs = st.bytes() / (ms_r * 1e-3) / 1e9
-    res["layer8b_decode_M64"] = {"GB/s": round(gbs, 2), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                                 "us": round(ms_r * 1e3, 2), "algorithmic_bytes": st.bytes(),
-                                 "plain_us": round(ms_p * 1e3, 2),
-                                 "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
-    for l in lins:
-        l.copies = []
-    st = Step(rl, torch, lins, [4096])
-    ms_r = time_slots(torch, lambda s: st.enqueue(s, batched=True), 2, 2, 6, 2)
-    ms_p = time_slots(torch, lambda s: st.enqueue(s, rotated=False, batched=True), 2, 2, 6, 2)
-    tf = st.flops() / (ms_r * 1e-3) / 1e12
-    res["layer8b_prefill_M4096"] = {"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                                    "us": round(ms_r * 1e3, 2),
-                                    "plain_TFLOP/s": round(st.flops() / (ms_p * 1e-3) / 1e12, 2),
-                                    "overhead_pct": round((ms_r - ms_p) / ms_p * 100, 2)}
+            "realizable_decode_step": name == "layered",
+            "launch": "4 dependent paro_linear_batch calls per layer (q/k/v, o, gate/up, down), 112 per step: "
+                      "the order of a real decode step" if name == "layered" else
+                      "one paro_linear_batch call for all 196 linears as independent calls (not a realizable "
+                      "decode step: the layers depend on each other)"}
     return res
 
 

@@ -165,7 +165,10 @@ size_t paro_workspace_bytes(int M, int D, int N);
  * fake quantization to a real TensorRT engine": one group-wise INT4 GEMM per
  * layer): y[m][n] = sum_g scale[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g]),
  * products of float16 values exact, accumulation in float32, y stored as
- * ydtype (PARO_F16 rounds once). x float16 [M][D]; y [M][N] must not overlap
+ * ydtype (PARO_F16 rounds once). A group whose scale is zero contributes
+ * nothing, as the formula says (paro_pack_weights never writes one: its scales
+ * are at least fp16(1e-5)); a non-finite scale makes the outputs it reaches
+ * non-finite. x float16 [M][D]; y [M][N] must not overlap
  * any input. ws is an optional device buffer: given at least
  * paro_workspace_bytes(M, D, N) bytes (which must not overlap any operand), a
  * prefill-shaped call may split its reduction over D and keep the partial sums

@@ -143,17 +143,39 @@ def _ptr(t) -> ctypes.c_void_p:
 
 
 def _want(t, dtype, shape, name):
+    """Type, dtype, shape and contiguity of one tensor argument (inputs, outputs and workspaces
+    alike); where it lives is checked by _on_gpu once every argument has passed this."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must live on the GPU")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(named):
+    """Every tensor of ``named`` (name -> tensor or None) lives on one and the same GPU."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must live on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+    return dev
+
+
+def _want_ws(ws):
+    """A workspace: a contiguous one-dimensional uint8 tensor (its numel is its byte count)."""
+    if ws is None:
+        return
+    _want(ws, _torch().uint8, (ws.numel(),), "ws")
 
 
 def _host_transform(pairs, theta, scale):
@@ -224,38 +246,39 @@ def paro_rotation_prepare(pairs, theta, scale, device="cuda") -> Rotation:
 
 
 def paro_pack_weights(rot: Rotation, W, out=None):
-    """W float16 [N][D] on the GPU -> (qweight uint8 [N][D/2], scales f16 [N][D/128], zeros f16 [N][D/128])."""
+    """W float16 [N][D] on the GPU -> (qweight uint8 [N][D/2], scales f16 [N][D/128], zeros f16 [N][D/128]).
+    ``out``: an optional (qweight, scales, zeros) tuple of tensors of those shapes to write."""
     torch = _torch()
     N, D = int(W.shape[0]), rot.D
     _want(W, torch.float16, (N, D), "W")
-    if out is None:
-        qw = torch.empty((N, D // 2), dtype=torch.uint8, device=W.device)
-        sc = torch.empty((N, D // GROUP), dtype=torch.float16, device=W.device)
-        z = torch.empty((N, D // GROUP), dtype=torch.float16, device=W.device)
-    else:
+    if out is not None:
         qw, sc, z = out
-    with torch.cuda.device(W.device):
-        _check(_lib.paro_pack_weights(rot.ptr, N, _ptr(W), _ptr(qw), _ptr(sc), _ptr(z), _stream_ptr(W.device)),
+        _want(qw, torch.uint8, (N, D // 2), "qweight")
+        _want(sc, torch.float16, (N, D // GROUP), "scales")
+        _want(z, torch.float16, (N, D // GROUP), "zeros")
+    dev = _on_gpu({"W": W, **({"qweight": qw, "scales": sc, "zeros": z} if out is not None else {})})
+    if out is None:
+        qw = torch.empty((N, D // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((N, D // GROUP), dtype=torch.float16, device=dev)
+        z = torch.empty((N, D // GROUP), dtype=torch.float16, device=dev)
+    with torch.cuda.device(dev):
+        _check(_lib.paro_pack_weights(rot.ptr, N, _ptr(W), _ptr(qw), _ptr(sc), _ptr(z), _stream_ptr(dev)),
                "paro_pack_weights")
     return qw, sc, z
 
 
 def paro_rotate(rot: Rotation, x, out=None):
-    """x float16 [M][D] -> transformed activations float16 [M][D]."""
+    """x float16 [M][D] -> transformed activations float16 [M][D] (``out``: a tensor of that shape)."""
     torch = _torch()
     M = int(x.shape[0])
     _want(x, torch.float16, (M, rot.D), "x")
-    xo = torch.empty_like(x) if out is None else out
-    with torch.cuda.device(x.device):
-        _check(_lib.paro_rotate(rot.ptr, M, _ptr(x), _ptr(xo), _stream_ptr(x.device)), "paro_rotate")
-    return xo
-
-
-def _linear_out(M, N, out_dtype, device, out):
-    torch = _torch()
     if out is not None:
-        return out
-    return torch.empty((M, N), dtype=out_dtype, device=device)
+        _want(out, torch.float16, (M, rot.D), "out")
+    dev = _on_gpu({"x": x, "out": out})
+    xo = torch.empty_like(x) if out is None else out
+    with torch.cuda.device(dev):
+        _check(_lib.paro_rotate(rot.ptr, M, _ptr(x), _ptr(xo), _stream_ptr(dev)), "paro_rotate")
+    return xo
 
 
 def _ydt(t):
@@ -267,22 +290,36 @@ def _ydt(t):
     raise TypeError("y must be float16 or float32")
 
 
-def paro_w4a16_linear(x, qweight, scales, zeros, out_dtype=None, out=None, ws=None):
-    """Plain group-wise INT4 linear: y = x . dequant(qweight, scales, zeros)^T."""
+def _linear_operands(x, qweight, scales, zeros, D, out, out_dtype, ws, what="x"):
+    """Check one linear's operands (and a given output / workspace); returns (M, N, y dtype)."""
     torch = _torch()
-    M, D = int(x.shape[0]), int(x.shape[1])
-    N = int(qweight.shape[0])
-    _want(x, torch.float16, (M, D), "x")
+    M, N = int(x.shape[0]), int(qweight.shape[0])
+    _want(x, torch.float16, (M, D), what)
     _want(qweight, torch.uint8, (N, D // 2), "qweight")
     _want(scales, torch.float16, (N, D // GROUP), "scales")
     _want(zeros, torch.float16, (N, D // GROUP), "zeros")
-    y = _linear_out(M, N, out_dtype or torch.float16, x.device, out)
+    dtype = out_dtype or (out.dtype if out is not None else torch.float16)
+    if dtype not in (torch.float16, torch.float32):
+        raise TypeError("y must be float16 or float32")
+    if out is not None:
+        _want(out, dtype, (M, N), "out")
+    _want_ws(ws)
+    return M, N, dtype
+
+
+def paro_w4a16_linear(x, qweight, scales, zeros, out_dtype=None, out=None, ws=None):
+    """Plain group-wise INT4 linear: y = x . dequant(qweight, scales, zeros)^T."""
+    torch = _torch()
+    D = int(x.shape[1]) if x.dim() == 2 else -1
+    M, N, dtype = _linear_operands(x, qweight, scales, zeros, D, out, out_dtype, ws)
+    dev = _on_gpu({"x": x, "qweight": qweight, "scales": scales, "zeros": zeros, "out": out, "ws": ws})
+    y = torch.empty((M, N), dtype=dtype, device=dev) if out is None else out
     need = _lib.paro_workspace_bytes(M, D, N)
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
-    with torch.cuda.device(x.device):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
         _check(_lib.paro_w4a16_linear(M, D, N, _ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), _ydt(y),
-                                      _ptr(ws), ws.numel() if ws is not None else 0, _stream_ptr(x.device)),
+                                      _ptr(ws), ws.numel() if ws is not None else 0, _stream_ptr(dev)),
                "paro_w4a16_linear")
     return y
 
@@ -290,20 +327,16 @@ def paro_w4a16_linear(x, qweight, scales, zeros, out_dtype=None, out=None, ws=No
 def paro_rotated_linear(rot: Rotation, x, qweight, scales, zeros, out_dtype=None, out=None, ws=None):
     """Fused runtime path: y = transform(x) . dequant(qweight, scales, zeros)^T."""
     torch = _torch()
-    M, D = int(x.shape[0]), rot.D
-    N = int(qweight.shape[0])
-    _want(x, torch.float16, (M, D), "x")
-    _want(qweight, torch.uint8, (N, D // 2), "qweight")
-    _want(scales, torch.float16, (N, D // GROUP), "scales")
-    _want(zeros, torch.float16, (N, D // GROUP), "zeros")
-    y = _linear_out(M, N, out_dtype or torch.float16, x.device, out)
+    D = rot.D
+    M, N, dtype = _linear_operands(x, qweight, scales, zeros, D, out, out_dtype, ws)
+    dev = _on_gpu({"x": x, "qweight": qweight, "scales": scales, "zeros": zeros, "out": out, "ws": ws})
+    y = torch.empty((M, N), dtype=dtype, device=dev) if out is None else out
     need = _lib.paro_workspace_bytes(M, D, N)
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
-    with torch.cuda.device(x.device):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
         _check(_lib.paro_rotated_linear(rot.ptr, M, N, _ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y),
-                                        _ydt(y), _ptr(ws), ws.numel() if ws is not None else 0,
-                                        _stream_ptr(x.device)),
+                                        _ydt(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream_ptr(dev)),
                "paro_rotated_linear")
     return y
 
@@ -316,29 +349,31 @@ def paro_linear_batch(calls, out_dtype=None, outs=None, ws=None):
     `outs` gives them)."""
     torch = _torch()
     n = len(calls)
-    arr = (paro_linear_args * max(n, 1))()
-    ys, keep = [], []
+    if outs is not None and len(outs) != n:
+        raise ValueError(f"outs has {len(outs)} tensors for {n} calls")
     dtype = out_dtype or (outs[0].dtype if outs else torch.float16)
-    device = None
+    shapes, named = [], {}
     for i, (rot, x, qweight, scales, zeros) in enumerate(calls):
-        M, D = int(x.shape[0]), int(x.shape[1])
-        N = int(qweight.shape[0])
+        D = int(x.shape[1]) if x.dim() == 2 else -1
         if rot is not None and rot.D != D:
             raise ValueError(f"call {i}: x has {D} channels, the transform {rot.D}")
-        _want(x, torch.float16, (M, D), "x")
-        _want(qweight, torch.uint8, (N, D // 2), "qweight")
-        _want(scales, torch.float16, (N, D // GROUP), "scales")
-        _want(zeros, torch.float16, (N, D // GROUP), "zeros")
-        y = _linear_out(M, N, dtype, x.device, outs[i] if outs else None)
-        if y.dtype != dtype:
-            raise TypeError("every output of a batch has the same dtype")
-        device = x.device
+        M, N, _ = _linear_operands(x, qweight, scales, zeros, D, outs[i] if outs else None, dtype, None,
+                                   what=f"calls[{i}].x")
+        shapes.append((M, D, N))
+        named.update({f"calls[{i}].x": x, f"calls[{i}].qweight": qweight, f"calls[{i}].scales": scales,
+                      f"calls[{i}].zeros": zeros, f"outs[{i}]": outs[i] if outs else None})
+    _want_ws(ws)
+    named["ws"] = ws
+    if n == 0:
+        return []
+    device = _on_gpu(named)
+    arr = (paro_linear_args * n)()
+    ys = []
+    for i, ((rot, x, qweight, scales, zeros), (M, D, N)) in enumerate(zip(calls, shapes)):
+        y = outs[i] if outs else torch.empty((M, N), dtype=dtype, device=device)
         ys.append(y)
-        keep.append(rot)
         arr[i] = paro_linear_args(ctypes.pointer(rot.handle) if rot is not None else None, M, D, N, x.data_ptr(),
                                   qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), y.data_ptr())
-    if n == 0:
-        return ys
     need = _lib.paro_linear_batch_workspace_bytes(n, arr)
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=device)

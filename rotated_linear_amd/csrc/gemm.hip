@@ -65,7 +65,7 @@ struct Tile {
   static constexpr int B_LD = (BN * 2 + kThreads - 1) / kThreads;  // 16-byte B chunks per thread per stage
   static constexpr size_t A_BYTES = size_t(BM) * kLdaH * 2;
   static constexpr size_t B_BYTES = size_t(BN) * kLdbB;
-  static constexpr size_t Z_BYTES = size_t(BN) * 8;  // two float16 pairs per column
+  static constexpr size_t Z_BYTES = size_t(BN) * 16;  // two float16 pairs and the nibble mask per column
   static constexpr size_t R_BYTES = size_t(BN) * 4;  // float32 ratio per column
   static constexpr size_t BUF = A_BYTES + B_BYTES + Z_BYTES + R_BYTES;
   static constexpr size_t LDS = 2 * BUF;
@@ -80,9 +80,10 @@ __device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
 }
 
 // 8 nibbles of one 32-bit word -> exact (q - z) as float16 in the order [0,4,1,5,2,6,3,7].
-// zlo = -(1024 + z) and zhi = -(64 + z) as float16 pairs.
-__device__ inline h8 dequant_word(uint32_t u, h2 zlo, h2 zhi) {
-  const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, e = 0x64006400u;
+// zlo = -(1024 + z) and zhi = -(64 + z) as float16 pairs; m0 = 0x000F000F, or 0 for a group whose
+// scale is zero (every nibble then reads as 0 and z as 0: the group contributes nothing).
+__device__ inline h8 dequant_word(uint32_t u, h2 zlo, h2 zhi, uint32_t m0) {
+  const uint32_t m1 = m0 << 4, e = 0x64006400u;
   const h2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
   const uint32_t v = u >> 8;
   const h2 a0 = __builtin_bit_cast(h2, and_or(u, m0, e)) + zlo;
@@ -199,16 +200,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int b) {
         *reinterpret_cast<uint4*>(Bs + (e >> 1) * kLdbB + (e & 1) * 16) = s.b[i];
     }
     if (tid < BN) {
-      if ((j & 1) == 0) {  // a group's first stage: the ratio to the previous group's scale
-        const float cur = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(s.s)));
-        Rs[tid] = j == 0 ? 1.f : prev_s / cur;
-        prev_s = cur;
+      // The accumulators hold the sums in units of the last nonzero group scale seen (prev_s, 1
+      // before any): a group with a nonzero scale first rescales them by prev_s / scale; a zero
+      // scale keeps them (ratio 1) and masks the group's codes, which is the group's exact
+      // contribution, 0.
+      const float cur = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(s.s)));
+      const bool zero = cur == 0.f;
+      if ((j & 1) == 0) {  // a group's first stage
+        Rs[tid] = (j == 0 || zero) ? 1.f : prev_s / cur;
+        if (!zero) prev_s = cur;
       }
-      const _Float16 z = __builtin_bit_cast(_Float16, uint16_t(s.z));
+      const _Float16 z = zero ? static_cast<_Float16>(0.0f) : __builtin_bit_cast(_Float16, uint16_t(s.z));
       const _Float16 zl = -(static_cast<_Float16>(1024.0f) + z), zh = -(static_cast<_Float16>(64.0f) + z);
       const h2 zl2 = {zl, zl}, zh2 = {zh, zh};
-      Zs[2 * tid] = __builtin_bit_cast(uint32_t, zl2);
-      Zs[2 * tid + 1] = __builtin_bit_cast(uint32_t, zh2);
+      reinterpret_cast<uint4*>(Zs)[tid] =
+          uint4{__builtin_bit_cast(uint32_t, zl2), __builtin_bit_cast(uint32_t, zh2), zero ? 0u : 0x000F000Fu, 0u};
     }
   };
 
@@ -230,12 +236,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int b) {
     const float* Rs = reinterpret_cast<const float*>(base + T::A_BYTES + T::B_BYTES + T::Z_BYTES);
     uint4 bw[T::TN];
     h2 zl[T::TN], zh[T::TN];
+    uint32_t mk[T::TN];
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
       const int n = wn * (BN / T::WN) + j * 32 + l32;
       bw[j] = *reinterpret_cast<const uint4*>(Bs + n * kLdbB + hh * 16);
-      zl[j] = __builtin_bit_cast(h2, Zs[2 * n]);
-      zh[j] = __builtin_bit_cast(h2, Zs[2 * n + 1]);
+      const uint4 zw = reinterpret_cast<const uint4*>(Zs)[n];
+      zl[j] = __builtin_bit_cast(h2, zw.x);
+      zh[j] = __builtin_bit_cast(h2, zw.y);
+      mk[j] = zw.z;
     }
     if (group_start) {
 #pragma unroll
@@ -257,7 +266,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int b) {
 #pragma unroll
       for (int j = 0; j < T::TN; ++j) {
         const uint32_t u = kk == 0 ? bw[j].x : kk == 1 ? bw[j].y : kk == 2 ? bw[j].z : bw[j].w;
-        const h8 bf = dequant_word(u, zl[j], zh[j]);
+        const h8 bf = dequant_word(u, zl[j], zh[j], mk[j]);
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][j], 0, 0, 0);
@@ -529,7 +538,8 @@ namespace {
 GemmArgs make_args(int M, int D, int N, const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                    const uint16_t* zeros, void* y, int ldy, int ydtype, void* ws, size_t ws_bytes, GemmPlan& g) {
   g = plan_gemm(M, D, N);
-  if (g.splits > 1 && ws_bytes < size_t(g.splits) * M * N * 4) g.splits = 1;  // no room for partials
+  // no room for the partial sums (the same rounded size gemm_workspace_bytes reports)
+  if (g.splits > 1 && ws_bytes < align256(size_t(g.splits) * M * N * 4)) g.splits = 1;
   GemmArgs a;
   a.x = x;
   a.qw = qweight;

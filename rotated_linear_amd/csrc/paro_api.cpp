@@ -237,10 +237,13 @@ paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t*
   if (paro_status s = check_linear_args(M, D, N, x, qweight, scales, zeros, y, ydtype)) return s;
   if (M == 0 || N == 0) return PARO_OK;
   const size_t need = linear_ws_bytes(M, D, N);
-  if (!ws) ws_bytes = 0;
-  if (need && ws_bytes >= need) {  // room for the split partial sums: they must not overlap any operand
+  if (need && ws && ws_bytes >= need) {  // room for the split partial sums: they must not overlap any operand
     if (!aligned16(ws)) return PARO_EINVAL;
     if (ws_overlaps(ws, need, M, D, N, x, qweight, scales, zeros, y, ydtype)) return PARO_EINVAL;
+    ws_bytes = need;
+  } else {  // too small (or none): the kernels never see a workspace that was not checked
+    ws = nullptr;
+    ws_bytes = 0;
   }
   return run_linear(M, D, N, static_cast<const uint16_t*>(x), false, qweight, static_cast<const uint16_t*>(scales),
                     static_cast<const uint16_t*>(zeros), y, ydtype, ws, ws_bytes, static_cast<hipStream_t>(stream));

@@ -26,16 +26,28 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_is_read_only_for_matching_sources(tmp_path, monkeypatch):
     b = load_bench()
-    f = tmp_path / "traffic.md"
-    monkeypatch.setattr(b, "TRAFFIC_FILE", str(f))
-    f.write_text("x\nsource_sha256_16 = %s\ntraffic_bytes_per_launch = 1234.0\n" % b.kernel_source_hash())
-    assert b.measured_traffic() == 1234
-    f.write_text("source_sha256_16 = 0000000000000000\ntraffic_bytes_per_launch = 1234.0\n")
-    assert b.measured_traffic() is None
-    f.write_text("source_sha256_16 = %s\n" % b.kernel_source_hash())  # no figure
-    assert b.measured_traffic() is None
-    monkeypatch.setattr(b, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
-    assert b.measured_traffic() is None
+    for which in ("decode", "prefill"):
+        f = tmp_path / f"traffic_{which}.md"
+        monkeypatch.setitem(b.TRAFFIC_FILES, which, str(f))
+        f.write_text("x\nsource_sha256_16 = %s\ntraffic_bytes_per_launch = 1234.0\n" % b.kernel_source_hash(which))
+        assert b.measured_traffic(which) == 1234
+        f.write_text("source_sha256_16 = 0000000000000000\ntraffic_bytes_per_launch = 1234.0\n")
+        assert b.measured_traffic(which) is None
+        f.write_text("source_sha256_16 = %s\n" % b.kernel_source_hash(which))  # no figure
+        assert b.measured_traffic(which) is None
+        monkeypatch.setitem(b.TRAFFIC_FILES, which, str(tmp_path / "missing.md"))
+        assert b.measured_traffic(which) is None
+
+
+def test_divisor_and_byte_counts():
+    b = load_bench()
+    assert b._divisor_at_most(20, 8) == 5 and b._divisor_at_most(20, 4) == 4 and b._divisor_at_most(7, 4) == 1
+    import workloads as W
+    # the survey's algorithmic bytes: weights + fp16 scale and zero + x + y + int16 pair index and fp32
+    # angle per channel per stage (4 K D) + fp32 channel scale (4 D)
+    M, D, N, K = 64, 4096, 14336, 8
+    assert W.algorithmic_bytes(M, D, N, K) == N * D // 2 + N * D // 32 + 2 * M * D + 2 * M * N + 4 * K * D + 4 * D
+    assert W.plain_bytes(M, D, N) == N * D // 2 + N * D // 32 + 2 * M * D + 2 * M * N
 
 
 def test_sclk_parser(tmp_path, monkeypatch):

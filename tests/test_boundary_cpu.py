@@ -293,3 +293,50 @@ def test_import_fails_loudly_without_the_library(tmp_path):
                        text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libparo.so is missing" in r.stderr
+
+
+def test_binding_checks_outputs_and_workspaces_before_launch():
+    """The binding checks every output and workspace tensor (shape, dtype, contiguity) as it does
+    the inputs, before any library call: an undersized or strided buffer would otherwise be
+    written past its end on the device. Here every tensor lives on the CPU, so a call that got
+    past the checks would stop at the device check ("must live on the GPU")."""
+    import torch
+
+    D, N, M = 256, 40, 3
+    rot = rl.Rotation(2, D, None, rl.paro_rotation(2, D, FAKE))
+    x = torch.zeros((M, D), dtype=torch.float16)
+    qw = torch.zeros((N, D // 2), dtype=torch.uint8)
+    sc = torch.zeros((N, D // 128), dtype=torch.float16)
+    z = torch.zeros((N, D // 128), dtype=torch.float16)
+    good_out = torch.zeros((M, N), dtype=torch.float16)
+
+    def raises(fn, kind, text):
+        with pytest.raises(kind, match=text):
+            fn()
+
+    for call in (lambda **k: rl.paro_w4a16_linear(x, qw, sc, z, **k),
+                 lambda **k: rl.paro_rotated_linear(rot, x, qw, sc, z, **k)):
+        raises(lambda: call(out=torch.zeros((M, N - 1), dtype=torch.float16)), ValueError, "out must have shape")
+        raises(lambda: call(out=torch.zeros((M + 1, N), dtype=torch.float16)), ValueError, "out must have shape")
+        raises(lambda: call(out=torch.zeros((N, M), dtype=torch.float16).t()), ValueError, "contiguous")
+        raises(lambda: call(out=torch.zeros((M, N), dtype=torch.bfloat16)), TypeError, "float16 or float32")
+        raises(lambda: call(out=good_out, out_dtype=torch.float32), TypeError, "out must be")
+        raises(lambda: call(out=good_out, ws=torch.zeros(512, dtype=torch.float32)), TypeError, "ws must be")
+        raises(lambda: call(out=good_out, ws=torch.zeros((2, 256), dtype=torch.uint8)), ValueError, "ws must have")
+        raises(lambda: call(out=good_out, ws=torch.zeros(1024, dtype=torch.uint8)[::2]), ValueError, "contiguous")
+        raises(lambda: call(out=good_out), ValueError, "must live on the GPU")
+    raises(lambda: rl.paro_rotate(rot, x, out=torch.zeros((M, D - 2), dtype=torch.float16)), ValueError,
+           "out must have shape")
+    raises(lambda: rl.paro_rotate(rot, x, out=torch.zeros((M, D), dtype=torch.float32)), TypeError, "out must be")
+    W = torch.zeros((N, D), dtype=torch.float16)
+    raises(lambda: rl.paro_pack_weights(rot, W, out=(qw[:-1], sc, z)), ValueError, "qweight must have shape")
+    raises(lambda: rl.paro_pack_weights(rot, W, out=(qw, sc.float(), z)), TypeError, "scales must be")
+    raises(lambda: rl.paro_pack_weights(rot, W, out=(qw, sc, z[:, :1])), ValueError, "zeros must have shape")
+    raises(lambda: rl.paro_pack_weights(rot, W, out=(qw, sc, z)), ValueError, "must live on the GPU")
+    calls = [(rot, x, qw, sc, z), (None, x, qw, sc, z)]
+    raises(lambda: rl.paro_linear_batch(calls, outs=[good_out]), ValueError, "outs has 1 tensors")
+    raises(lambda: rl.paro_linear_batch(calls, outs=[good_out, torch.zeros((M, N + 1), dtype=torch.float16)]),
+           ValueError, "out must have shape")
+    raises(lambda: rl.paro_linear_batch(calls, outs=[good_out, good_out.float()]), TypeError, "out must be")
+    raises(lambda: rl.paro_linear_batch(calls, ws=torch.zeros(64, dtype=torch.int8)), TypeError, "ws must be")
+    raises(lambda: rl.paro_linear_batch(calls, outs=[good_out, good_out.clone()]), ValueError, "must live on the GPU")

@@ -2,13 +2,16 @@
 
 Bars:
   * pack: qweight bytes, scales and zeros bit-identical to the oracle;
-  * rotate: every element within ``rotate_bound`` of the float64 transform, and at
-    most 2% of elements off the float16 rounding of the float64 transform;
+  * rotate: every element within ``rotate_bound`` of the float64 transform, and few
+    elements off the float16 rounding of the float64 transform (``C.rotate_off_cap``: an
+    emulation of the kernel's float32 sequence puts 0.06% of elements off at K = 8, growing
+    about linearly with K);
   * linears (spec bar): max-abs <= 1e-2 and relative L2 <= 2e-3, with the
     float32-output epilogue, against the oracle applied to the same dequantized
     weights and -- for the rotated linear -- the same float16 activations the
     GEMM consumes (f16_rne of the float64 transform); the production float16
-    output is also held to relative L2 <= 2e-3 against the unrounded float64 path.
+    output is also held to relative L2 <= 2e-3 against the unrounded float64 path, and to
+    max-abs <= 1e-2 on the outputs with |y| < 16 (above, one float16 spacing exceeds 1e-2).
 Full-size workloads are checked on sampled weight rows / token rows, always
 including the first and last (ragged) ones.
 """
@@ -95,9 +98,15 @@ def _check_rotate(L, x):
     err = np.abs(got - a)
     worst = float((err / bound).max())
     assert worst <= 1.0, f"rotate error {worst:.3f}x the bound"
-    off = float((got != O.f16_rne(a).astype(np.float64)).mean())
-    assert off <= 0.02, f"{off:.4%} of elements off the float16 rounding of the float64 transform"
+    _check_off_rate(got, a, L.spec.K)
     return got
+
+
+def _check_off_rate(got, a, K):
+    off = int((got != O.f16_rne(a).astype(np.float64)).sum())
+    cap = C.rotate_off_cap(a.size, K)
+    C.log(f"  rotate: {off} of {a.size} elements ({off / a.size:.4%}) off fp16(float64 transform), cap {cap}")
+    assert off <= cap, f"{off} of {a.size} elements off the float16 rounding of the float64 transform (cap {cap})"
 
 
 ROT_CASES = [(1, 0, 4), (2, 0, 1), (2, 1, 4), (2, 3, 16), (3, 0, 1), (3, 0, 16), (3, 0, 256), (4, 0, 2048),
@@ -116,6 +125,7 @@ def test_rotate_parity(wid, index, M):
         a = O.transform_activations(x[rows], L.pairs, L.theta, L.scale)
         bound = C.rotate_bound(a, x[rows].astype(np.float64), L.scale, L.spec.K)
         assert float((np.abs(got[rows] - a) / bound).max()) <= 1.0
+        _check_off_rate(got[rows], a, L.spec.K)
     else:
         _check_rotate(L, x)
 
@@ -177,6 +187,8 @@ def _linear_case(L, M, rows_w, oracle_pack, gpu_weights):
     assert mx <= C.MAX_ABS and rel <= C.REL_L2, f"rotated linear (fp32 out): max-abs {mx:.3e} rel-L2 {rel:.3e}"
     mx2, rel2 = C.linear_metrics(y16[:, rows_w], ref_exact)
     assert rel2 <= C.REL_L2, f"rotated linear (fp16 out vs float64 path): rel-L2 {rel2:.3e} (max-abs {mx2:.3e})"
+    mx16 = C.masked_max_abs(y16[:, rows_w], ref_exact, 16.0)
+    assert mx16 <= C.MAX_ABS, f"rotated linear (fp16 out vs float64 path): max-abs {mx16:.3e} where |y| < 16"
     mx3, rel3 = C.linear_metrics(p32[:, rows_w], ref_plain)
     assert mx3 <= C.MAX_ABS and rel3 <= C.REL_L2, f"w4a16 linear: max-abs {mx3:.3e} rel-L2 {rel3:.3e}"
     return mx, rel, mx2, rel2
@@ -206,11 +218,16 @@ def test_linear_parity(wid, index, M):
         xd = C.dev(x, torch)
         rot = _rot(L)
         y32 = C.host(rl.paro_rotated_linear(rot, xd, *gpu_w, out_dtype=torch.float32))[x_rows][:, rows_w]
+        y16 = C.host(rl.paro_rotated_linear(rot, xd, *gpu_w, out_dtype=torch.float16))[x_rows][:, rows_w]
         p32 = C.host(rl.paro_w4a16_linear(xd, *gpu_w, out_dtype=torch.float32))[x_rows][:, rows_w]
         a = O.transform_activations(x[x_rows], Lm.pairs, Lm.theta, Lm.scale)
         deq = O.dequantize(*oracle_pack)
         mx, rel = C.linear_metrics(y32, O.f16_rne(a).astype(np.float64) @ deq.T)
         assert mx <= C.MAX_ABS and rel <= C.REL_L2, f"rotated linear: max-abs {mx:.3e} rel-L2 {rel:.3e}"
+        ref_exact = a @ deq.T
+        mx2, rel2 = C.linear_metrics(y16, ref_exact)
+        mx16 = C.masked_max_abs(y16, ref_exact, 16.0)
+        assert rel2 <= C.REL_L2 and mx16 <= C.MAX_ABS, f"fp16 out: rel-L2 {rel2:.3e}, max-abs {mx16:.3e} where |y| < 16"
         mx3, rel3 = C.linear_metrics(p32, x[x_rows].astype(np.float64) @ deq.T)
         assert mx3 <= C.MAX_ABS and rel3 <= C.REL_L2, f"w4a16 linear: max-abs {mx3:.3e} rel-L2 {rel3:.3e}"
         C.log(f"  max-abs {mx:.2e} rel-L2 {rel:.2e}")

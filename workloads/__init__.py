@@ -195,10 +195,17 @@ def custom_linear(seed: int, M: int, D: int, N: int, K: int, x_outlier_frac=0.00
 
 def algorithmic_bytes(M: int, D: int, N: int, K: int, out_bytes: int = 2) -> int:
     """Bytes the fused rotated linear must move: packed weights, fp16 scale and zero
-    per 128-group, x in, y out, and the transform parameters (int16 pair indices,
-    fp32 cos/sin per pair per stage, fp32 1/s per channel)."""
+    per 128-group, x in, y out, and the transform's parameters -- per stage one int16
+    pair index per channel and one fp32 angle per pair (4 K D bytes), and one fp32
+    channel scale per channel (4 D bytes)."""
     w = N * D // 2 + N * (D // GROUP) * 4
-    return w + 2 * M * D + out_bytes * M * N + 6 * K * D + 4 * D
+    return w + 2 * M * D + out_bytes * M * N + 4 * K * D + 4 * D
+
+
+def transform_bytes(M: int, D: int, K: int) -> int:
+    """Bytes the standalone transform must move: x in, x' out (fp16) and the transform's
+    parameters as in ``algorithmic_bytes``."""
+    return 4 * M * D + 4 * K * D + 4 * D
 
 
 def plain_bytes(M: int, D: int, N: int, out_bytes: int = 2) -> int:
