@@ -82,6 +82,32 @@ def masked_max_abs(got: np.ndarray, ref: np.ndarray, below: float) -> float:
     return float(np.abs(got.astype(np.float64) - ref)[m].max()) if m.any() else 0.0
 
 
+def fp16_path_bound(a: np.ndarray, deq: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-output bound on |y16 - a . deq^T| for the float16 output of the rotated linear, where a is
+    the float64 transform and ref = a . deq^T. Three terms: rounding x' once to float16 moves each
+    output by at most e_x = |f16(a) - a| . |deq|^T (exact worst case, triangle inequality); the
+    float32 sums of exact products add at most e_acc = (128 + G + 4) 2^-24 |f16(a)| . |deq|^T (up to
+    128 additions inside a group, G = D/128 across groups, the scale multiplies); rounding the result
+    to float16 adds half a float16 spacing at |ref| + e_x + e_acc."""
+    a16 = f16_of(a)
+    G = a.shape[1] // 128
+    e_x = np.abs(a16 - a) @ np.abs(deq).T
+    e_acc = (128 + G + 4) * 2.0 ** -24 * (np.abs(a16) @ np.abs(deq).T)
+    return e_x + e_acc + 0.5 * ulp16(np.abs(ref) + e_x + e_acc)
+
+
+def over_bound(err: np.ndarray, bound: np.ndarray) -> float:
+    """max(err / bound), counting 0 / 0 as 0 (zero weight rows give zero error and bound) and any
+    error where the bound is 0 as infinite."""
+    err = np.abs(err)
+    r = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    return float(r.max()) if r.size else 0.0
+
+
+def f16_of(a: np.ndarray) -> np.ndarray:
+    return O.f16_rne(a).astype(np.float64)
+
+
 def linear_metrics(got: np.ndarray, ref: np.ndarray):
     err = np.abs(got.astype(np.float64) - ref)
     return float(err.max()), float(np.linalg.norm(got.astype(np.float64) - ref) / max(np.linalg.norm(ref), 1e-30))
