@@ -38,7 +38,9 @@
  *     N * D/128 is odd, the word holding the last element also covers the 2
  *     bytes after the array (never a separate page); they are not used.
  *   - The caller owns every buffer. The library allocates nothing, frees
- *     nothing and keeps no mutable global state; calls are re-entrant.
+ *     nothing and keeps no mutable global state; calls are re-entrant. The
+ *     one exception is paro_rotated_linear_noalloc's fixed scratch array (see
+ *     there), which every GPU the library runs on holds from load to exit.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     is asynchronous, except paro_rotation_prepare, which synchronizes
  *     `stream` once its upload is enqueued.
@@ -195,6 +197,25 @@ paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t*
 paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void* x,
                                 const uint8_t* qweight, const void* scales, const void* zeros,
                                 void* y, int ydtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * paro_rotated_linear_noalloc -- paro_rotated_linear for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as paro_rotated_linear, without a workspace argument: the
+ * call's workspace (paro_workspace_bytes(M, D, N) at most) is a fixed scratch array inside the
+ * library, paro_noalloc_max_bytes() = 64 MiB on every GPU the library runs on (held until the
+ * process ends). A call whose workspace would exceed it returns PARO_EWORKSPACE before
+ * anything is enqueued. The call allocates and frees nothing; its first call on a device looks
+ * up that device's scratch address once. Every call on one GPU shares that GPU's scratch, so
+ * calls that overlap in time on one GPU (two streams, two host threads) race; calls on one
+ * stream are ordered and safe. Nothing in the scratch needs to start at zero.
+ */
+paro_status paro_rotated_linear_noalloc(const paro_rotation* r, int M, int N, const void* x,
+                                        const uint8_t* qweight, const void* scales, const void* zeros,
+                                        void* y, int ydtype, void* stream);
+
+/* Bytes of the scratch array paro_rotated_linear_noalloc uses (its largest workspace). */
+size_t paro_noalloc_max_bytes(void);
 
 /* One linear of a batch: paro_rotated_linear(rot, ...) when rot != NULL (then D
  * must equal rot->D), else paro_w4a16_linear(M, D, N, ...). Pointers as there. */

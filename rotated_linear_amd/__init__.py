@@ -87,10 +87,15 @@ _lib.paro_rotated_linear.restype = _i
 _lib.paro_rotated_linear.argtypes = [ctypes.POINTER(paro_rotation), _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp,
                                      _sz, _vp]
 
+_lib.paro_rotated_linear_noalloc.restype = _i
+_lib.paro_rotated_linear_noalloc.argtypes = [ctypes.POINTER(paro_rotation), _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp]
+_lib.paro_noalloc_max_bytes.restype = _sz
+_lib.paro_noalloc_max_bytes.argtypes = []
+
 EXPORTS = ("paro_status_str", "paro_version", "paro_rotation_bytes", "paro_rotation_encode", "paro_rotation_prepare",
            "paro_pack_weights", "paro_rotate", "paro_workspace_bytes", "paro_w4a16_linear",
            "paro_rotated_linear", "paro_linear_batch_workspace_bytes",
-           "paro_linear_batch")
+           "paro_linear_batch", "paro_rotated_linear_noalloc", "paro_noalloc_max_bytes")
 
 
 class ParoError(RuntimeError):
@@ -339,6 +344,27 @@ def paro_rotated_linear(rot: Rotation, x, qweight, scales, zeros, out_dtype=None
                                         _ydt(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream_ptr(dev)),
                "paro_rotated_linear")
     return y
+
+
+def paro_noalloc_max_bytes() -> int:
+    return _lib.paro_noalloc_max_bytes()
+
+
+def paro_rotated_linear_noalloc(rot: Rotation, x, qweight, scales, zeros, out):
+    """paro_rotated_linear without a workspace: the library's fixed scratch array serves as the
+    workspace (for callers that cannot allocate). ``out`` (float16 or float32 [M][N]) is required,
+    so nothing is allocated here either."""
+    torch = _torch()
+    if out is None:
+        raise ValueError("out is required: this call allocates nothing")
+    D = rot.D
+    M, N, _ = _linear_operands(x, qweight, scales, zeros, D, out, None, None)
+    dev = _on_gpu({"x": x, "qweight": qweight, "scales": scales, "zeros": zeros, "out": out})
+    with torch.cuda.device(dev):
+        _check(_lib.paro_rotated_linear_noalloc(rot.ptr, M, N, _ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros),
+                                                _ptr(out), _ydt(out), _stream_ptr(dev)),
+               "paro_rotated_linear_noalloc")
+    return out
 
 
 def paro_linear_batch(calls, out_dtype=None, outs=None, ws=None):

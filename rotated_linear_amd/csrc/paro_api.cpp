@@ -274,6 +274,23 @@ paro_status paro_rotated_linear(const paro_rotation* r, int M, int N, const void
   return run_rotated_two_step(R, M, N, xh, qweight, sc, zr, y, ydtype, ws, need, st);
 }
 
+paro_status paro_rotated_linear_noalloc(const paro_rotation* r, int M, int N, const void* x,
+                                        const uint8_t* qweight, const void* scales, const void* zeros, void* y,
+                                        int ydtype, void* stream) {
+  if (paro_status s = check_rotation(r)) return s;
+  if (paro_status s = check_linear_args(M, r->D, N, x, qweight, scales, zeros, y, ydtype)) return s;
+  if (M == 0 || N == 0) return PARO_OK;
+  const size_t need = rotated_ws_bytes(r->K, M, r->D, N);
+  if (need > kScratchBytes) return PARO_EWORKSPACE;
+  void* ws = nullptr;
+  if (need) {  // the scratch array of this device (looked up on its first use there)
+    if (hipError_t e = scratch_buffer(&ws)) return from_hip(e);
+  }
+  return paro_rotated_linear(r, M, N, x, qweight, scales, zeros, y, ydtype, ws, need ? kScratchBytes : 0, stream);
+}
+
+size_t paro_noalloc_max_bytes(void) { return kScratchBytes; }
+
 // ---- batches -------------------------------------------------------------------------------
 
 // Calls up to this many rows have their transforms batched into shared launches.

@@ -168,4 +168,10 @@ struct GemmCall {
 };
 hipError_t launch_gemm_group(const GemmCall* calls, int n, int ydtype, hipStream_t st);
 
+// ---- the fixed scratch buffer of paro_rotated_linear_noalloc (noalloc.hip) ----
+constexpr size_t kScratchBytes = size_t(64) << 20;
+// This device's address of the scratch array (looked up once per device with the device
+// current, then kept); *ptr is 256-byte aligned and holds kScratchBytes bytes.
+hipError_t scratch_buffer(void** ptr);
+
 }  // namespace paro

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     out = subprocess.run(["nm", "-D", "--defined-only", rl.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(paro_\w+)", out))
     missing = [n for n in names if n not in exported]
