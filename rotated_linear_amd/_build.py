@@ -26,8 +26,9 @@ COMMON = [
 ]
 # per-file extras: the build-time pack must round every float64 product and sum on its own
 # the GEMM keeps its accumulators in architectural registers (the per-group rescale multiplies them)
-EXTRA = {"pack.hip": ["-ffp-contract=off"], "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
-SOURCES = ["paro_api.cpp", "schedule.cpp", "pack.hip", "rotate.hip", "decode.hip", "gemm.hip", "noalloc.hip"]
+EXTRA = {"pack.hip": ["-ffp-contract=off"], "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "skinny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCES = ["paro_api.cpp", "schedule.cpp", "pack.hip", "rotate.hip", "decode.hip", "gemm.hip", "skinny.hip", "noalloc.hip"]
 
 
 def _hipcc() -> str:

@@ -425,11 +425,6 @@ __device__ __forceinline__ void reduce_any(int S, const float* part, void* y, in
 
 // One reduction per launch (S uniform) or several, one per call of a group (each block
 // serves one call; S and the vector width are uniform per block).
-struct ReduceCall {
-  const float* part;
-  void* y;
-  int M, N, ldy, S, vec, blocks;
-};
 struct ReduceGroupArgs {
   ReduceCall c[kGemmGroupMax];
   int block0[kGemmGroupMax];
@@ -447,6 +442,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceGroupArg
   else
     reduce_any<false>(c.S, c.part, c.y, c.M, c.N, c.ldy, g.ydtype, item0, stride);
 }
+
+}  // namespace
 
 ReduceCall reduce_call(const float* part, void* y, int M, int N, int ldy, int S) {
   // 16-byte partial loads and 8- or 16-byte stores need N, ldy (and so every row start) in fours
@@ -473,6 +470,8 @@ hipError_t launch_reduce_group(const ReduceCall* calls, int n, int ydtype, hipSt
   }
   return hipSuccess;
 }
+
+namespace {
 
 template <int BM, int BN, int WM, int PD, bool APERM>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {

@@ -33,9 +33,11 @@ paro_status check_rotation(const paro_rotation* r) {
 
 paro_status from_hip(hipError_t e) { return e == hipSuccess ? PARO_OK : PARO_EHIP; }
 
-// Workspace of one plain linear: the GEMM's split partial sums (decode-shaped calls take none).
+// Workspace of one plain linear: the split partial sums of the skinny kernel (17..64 rows) or of
+// the GEMM (decode-shaped calls take none).
 size_t linear_ws_bytes(int M, int D, int N) {
   if (M <= 0 || N <= 0 || decode_takes(-1, M, D, N)) return 0;
+  if (skinny_takes(M, D, N)) return skinny_workspace_bytes(M, D, N);
   return gemm_workspace_bytes(M, D, N);
 }
 
@@ -213,6 +215,10 @@ static paro_status run_linear(int M, int D, int N, const uint16_t* x, bool x_nib
   if (decode_takes(-1, M, D, N)) {
     const DecodeCall c{nullptr, M, N, x, x_nibble_order, qweight, scales, zeros, y};
     return from_hip(launch_decode(D, ydtype, &c, 1, st));
+  }
+  if (skinny_takes(M, D, N)) {
+    const SkinnyJob j{M, D, N, x, x_nibble_order, qweight, scales, zeros, y, ws, ws_bytes};
+    return from_hip(launch_skinny(&j, 1, ydtype, st));
   }
   return from_hip(launch_gemm(M, D, N, x, x_nibble_order, qweight, scales, zeros, y, ydtype, ws, ws_bytes, st));
 }
@@ -420,9 +426,25 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
   // sharing a tiling run in one launch, their split reductions in one more (one such call
   // rarely fills the GPU; larger ones do, and run one at a time below)
   std::vector<GemmCall> gemms;
+  std::vector<SkinnyJob> skinny;
   for (int i = 0; i < count; ++i) {
     if (done[i] || (calls[i].rot && !rotated[i]) || calls[i].M > kBatchTransformMaxM) continue;
     const paro_linear_args& c = calls[i];
+    if (skinny_takes(c.M, c.D, c.N)) {  // 17..64 rows: one skinny launch for all of them
+      SkinnyJob j{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
+                  static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
+                  linear_ws_bytes(c.M, c.D, c.N)};
+      if (c.rot) {
+        const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
+        j.x = reinterpret_cast<const uint16_t*>(slice[i]);
+        j.x_nibble_order = true;
+        j.ws = slice[i] + xr_bytes;
+        j.ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+      }
+      skinny.push_back(j);
+      done[i] = 1;
+      continue;
+    }
     GemmCall g{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
                static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
                linear_ws_bytes(c.M, c.D, c.N)};
@@ -436,6 +458,8 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     gemms.push_back(g);
     done[i] = 1;
   }
+  if (!skinny.empty())
+    if (hipError_t e = launch_skinny(skinny.data(), int(skinny.size()), ydtype, st)) return from_hip(e);
   if (!gemms.empty())
     if (hipError_t e = launch_gemm_group(gemms.data(), int(gemms.size()), ydtype, st)) return from_hip(e);
   // the longer calls one at a time, a rotated call's transform right before its linear, whose

@@ -168,6 +168,47 @@ struct GemmCall {
 };
 hipError_t launch_gemm_group(const GemmCall* calls, int n, int ydtype, hipStream_t st);
 
+// The ordered split reduction (gemm.hip): y[m][n] = sum over s < S of part[s][m][n], added in split
+// order (deterministic), y rows ldy elements apart. One launch serves up to kGemmGroupMax calls.
+struct ReduceCall {
+  const float* part;
+  void* y;
+  int M, N, ldy, S, vec, blocks;
+};
+ReduceCall reduce_call(const float* part, void* y, int M, int N, int ldy, int S);
+hipError_t launch_reduce_group(const ReduceCall* calls, int n, int ydtype, hipStream_t st);
+
+// ---- linears of 17..64 rows (skinny.hip) ----
+constexpr int kSkinnyMaxM = 64;
+// Reductions longer than this many 128-channel groups are split over workgroups, and so are those
+// of calls too narrow to give kSkinnyMinUnits workgroups (256 columns each) otherwise.
+constexpr int kSkinnyMaxGroups = 32;
+constexpr int kSkinnyMinUnits = 16;
+// Calls one skinny launch carries in its kernel arguments.
+constexpr int kSkinnyMaxCalls = 16;
+struct SkinnyPlan {
+  int tiles, splits, gps;  // 256-column tiles, reduction splits, groups per split
+};
+// The tiling of a call: a function of its shape only (the same alone and in a batch).
+SkinnyPlan skinny_plan(int M, int D, int N);
+bool skinny_takes(int M, int D, int N);
+// Workspace a call needs for its split partial sums.
+size_t skinny_workspace_bytes(int M, int D, int N);
+struct SkinnyJob {
+  int M, D, N;
+  const uint16_t* x;
+  bool x_nibble_order;
+  const uint8_t* qweight;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  void* y;
+  void* ws;  // room for the split partial sums (skinny_workspace_bytes)
+  size_t ws_bytes;
+};
+// The calls sharing x's word order run as one launch (up to kSkinnyMaxCalls each), their split
+// reductions as one more.
+hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t st);
+
 // ---- the fixed scratch buffer of paro_rotated_linear_noalloc (noalloc.hip) ----
 constexpr size_t kScratchBytes = size_t(64) << 20;
 // This device's address of the scratch array (looked up once per device with the device
