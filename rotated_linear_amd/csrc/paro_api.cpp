@@ -1,8 +1,11 @@
 // Host side of libparo: argument validation, descriptor preparation and dispatch.
 // Every error path returns before anything is enqueued on the stream.
 #include <math.h>
+
+#include <algorithm>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "paro_internal.h"
@@ -72,6 +75,43 @@ bool ws_overlaps(const void* ws, size_t need, int M, int D, int N, const void* x
          overlap(ws, need, y, size_t(M) * size_t(N) * (ydtype == PARO_F32 ? 4 : 2)) ||
          overlap(ws, need, qweight, size_t(N) * D / 2) || overlap(ws, need, scales, size_t(N) * G * 2) ||
          overlap(ws, need, zeros, size_t(N) * G * 2);
+}
+
+// The batch's second lane: a stream of the library's own per device (default priority,
+// non-blocking) with a fork and a join event. paro_linear_batch runs independent groups of calls
+// on it concurrently with the caller's stream, ordered by the two events, so that (say) a long
+// transform of one group overlaps the linears of another. Created on the first batch that wants
+// it; never during a stream capture (the batch then runs on the caller's stream alone, computing
+// the same bits). g_side_mu is held from the fork to the join, so two host threads never
+// interleave one device's events.
+struct SideLane {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideLane g_side[kMaxDevices];
+
+bool side_lane_locked(hipStream_t st, SideLane** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  SideLane& L = g_side[dev];
+  if (!L.ok) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+    if (hipStreamCreateWithFlags(&L.side, hipStreamNonBlocking) != hipSuccess) return false;
+    if (hipEventCreateWithFlags(&L.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&L.join, hipEventDisableTiming) != hipSuccess) {
+      if (L.fork) (void)hipEventDestroy(L.fork);
+      (void)hipStreamDestroy(L.side);
+      L = SideLane{};
+      return false;
+    }
+    L.ok = true;
+  }
+  *out = &L;
+  return true;
 }
 
 }  // namespace
@@ -394,98 +434,144 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     slice[i] = wsp;
     wsp += c.rot ? rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) : linear_ws_bytes(c.M, c.D, c.N);
   }
+  // Two lanes: when the rotated calls still to run have several D, the calls of every D but the
+  // one with the most packed weight bytes (transforms and linears) run on the side lane,
+  // concurrently with the rest. Each call's kernels, tiling and summation order are the same in
+  // either lane, so the results do not depend on the split.
+  std::vector<char> lane(size_t(count > 0 ? count : 0), 0);
+  int n_side = 0;
+  {
+    std::vector<std::pair<int, size_t>> per_d;
+    for (int i = 0; i < count; ++i) {
+      if (done[i] || !calls[i].rot) continue;
+      const size_t wb = size_t(calls[i].N) * size_t(calls[i].D) / 2;
+      auto it = std::find_if(per_d.begin(), per_d.end(), [&](const std::pair<int, size_t>& e) { return e.first == calls[i].D; });
+      if (it == per_d.end())
+        per_d.emplace_back(calls[i].D, wb);
+      else
+        it->second += wb;
+    }
+    if (per_d.size() >= 2) {
+      const int d_main = std::max_element(per_d.begin(), per_d.end(), [](const std::pair<int, size_t>& a,
+                                                                         const std::pair<int, size_t>& b) {
+                           return a.second < b.second;
+                         })->first;
+      for (int i = 0; i < count; ++i)
+        if (!done[i] && calls[i].rot && calls[i].D != d_main) {
+          lane[i] = 1;
+          ++n_side;
+        }
+    }
+  }
   std::vector<char> rotated(size_t(count > 0 ? count : 0), 0);
-  for (int i = 0; i < count; ++i) {
-    if (done[i] || !calls[i].rot || rotated[i] || calls[i].M > kBatchTransformMaxM) continue;
-    std::vector<RotateJob> jobs;
-    for (int j = i; j < count; ++j) {
-      const paro_linear_args& c = calls[j];
-      if (done[j] || !c.rot || rotated[j] || c.D != calls[i].D || c.M > kBatchTransformMaxM) continue;
-      rots[j] = dev_rot(*c.rot);
-      jobs.push_back(RotateJob{&rots[j], c.M, static_cast<const uint16_t*>(c.x), reinterpret_cast<uint16_t*>(slice[j])});
-      rotated[j] = 1;
+  auto run_lane = [&](int ln, hipStream_t ls) -> paro_status {
+    for (int i = 0; i < count; ++i) {
+      if (done[i] || lane[i] != ln || !calls[i].rot || rotated[i] || calls[i].M > kBatchTransformMaxM) continue;
+      std::vector<RotateJob> jobs;
+      for (int j = i; j < count; ++j) {
+        const paro_linear_args& c = calls[j];
+        if (done[j] || lane[j] != ln || !c.rot || rotated[j] || c.D != calls[i].D || c.M > kBatchTransformMaxM) continue;
+        rots[j] = dev_rot(*c.rot);
+        jobs.push_back(RotateJob{&rots[j], c.M, static_cast<const uint16_t*>(c.x), reinterpret_cast<uint16_t*>(slice[j])});
+        rotated[j] = 1;
+      }
+      if (hipError_t e = launch_rotate_batch(jobs.data(), int(jobs.size()), true, ls)) return from_hip(e);
     }
-    if (hipError_t e = launch_rotate_batch(jobs.data(), int(jobs.size()), true, st)) return from_hip(e);
-  }
-  // decode-shaped linears whose transform just ran in a batch (D or K beyond what the decode
-  // kernel runs inside): one decode launch per D on the transformed x, as for the plain calls
-  for (int i = 0; i < count; ++i) {
-    if (done[i] || !rotated[i] || !decode_takes(-1, calls[i].M, calls[i].D, calls[i].N)) continue;
-    std::vector<DecodeCall> group;
-    for (int j = i; j < count; ++j) {
-      const paro_linear_args& c = calls[j];
-      if (done[j] || !rotated[j] || c.D != calls[i].D || !decode_takes(-1, c.M, c.D, c.N)) continue;
-      group.push_back(DecodeCall{nullptr, c.M, c.N, reinterpret_cast<const uint16_t*>(slice[j]), true, c.qweight,
-                                 static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
-                                 c.y});
-      done[j] = 1;
+    // decode-shaped linears whose transform just ran in a batch (D or K beyond what the decode
+    // kernel runs inside): one decode launch per D on the transformed x, as for the plain calls
+    for (int i = 0; i < count; ++i) {
+      if (done[i] || lane[i] != ln || !rotated[i] || !decode_takes(-1, calls[i].M, calls[i].D, calls[i].N)) continue;
+      std::vector<DecodeCall> group;
+      for (int j = i; j < count; ++j) {
+        const paro_linear_args& c = calls[j];
+        if (done[j] || lane[j] != ln || !rotated[j] || c.D != calls[i].D || !decode_takes(-1, c.M, c.D, c.N)) continue;
+        group.push_back(DecodeCall{nullptr, c.M, c.N, reinterpret_cast<const uint16_t*>(slice[j]), true, c.qweight,
+                                   static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
+                                   c.y});
+        done[j] = 1;
+      }
+      if (hipError_t e = launch_decode(calls[i].D, ydtype, group.data(), int(group.size()), ls)) return from_hip(e);
     }
-    if (hipError_t e = launch_decode(calls[i].D, ydtype, group.data(), int(group.size()), st)) return from_hip(e);
-  }
-  // GEMM-shaped linears of up to 256 rows, on x or on an already transformed x: the calls
-  // sharing a tiling run in one launch, their split reductions in one more (one such call
-  // rarely fills the GPU; larger ones do, and run one at a time below)
-  std::vector<GemmCall> gemms;
-  std::vector<SkinnyJob> skinny;
-  for (int i = 0; i < count; ++i) {
-    if (done[i] || (calls[i].rot && !rotated[i]) || calls[i].M > kBatchTransformMaxM) continue;
-    const paro_linear_args& c = calls[i];
-    if (skinny_takes(c.M, c.D, c.N)) {  // 17..64 rows: one skinny launch for all of them
-      SkinnyJob j{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
-                  static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
-                  linear_ws_bytes(c.M, c.D, c.N)};
+    // GEMM-shaped linears of up to 256 rows, on x or on an already transformed x: the calls
+    // sharing a tiling run in one launch, their split reductions in one more (one such call
+    // rarely fills the GPU; larger ones do, and run one at a time below)
+    std::vector<GemmCall> gemms;
+    std::vector<SkinnyJob> skinny;
+    for (int i = 0; i < count; ++i) {
+      if (done[i] || lane[i] != ln || (calls[i].rot && !rotated[i]) || calls[i].M > kBatchTransformMaxM) continue;
+      const paro_linear_args& c = calls[i];
+      if (skinny_takes(c.M, c.D, c.N)) {  // 17..64 rows: one skinny launch for all of them
+        SkinnyJob j{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
+                    static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
+                    linear_ws_bytes(c.M, c.D, c.N)};
+        if (c.rot) {
+          const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
+          j.x = reinterpret_cast<const uint16_t*>(slice[i]);
+          j.x_nibble_order = true;
+          j.ws = slice[i] + xr_bytes;
+          j.ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+        }
+        skinny.push_back(j);
+        done[i] = 1;
+        continue;
+      }
+      GemmCall g{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
+                 static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
+                 linear_ws_bytes(c.M, c.D, c.N)};
       if (c.rot) {
         const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
-        j.x = reinterpret_cast<const uint16_t*>(slice[i]);
-        j.x_nibble_order = true;
-        j.ws = slice[i] + xr_bytes;
-        j.ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+        g.x = reinterpret_cast<const uint16_t*>(slice[i]);
+        g.x_nibble_order = true;
+        g.ws = slice[i] + xr_bytes;
+        g.ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
       }
-      skinny.push_back(j);
+      gemms.push_back(g);
       done[i] = 1;
-      continue;
     }
-    GemmCall g{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
-               static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
-               linear_ws_bytes(c.M, c.D, c.N)};
-    if (c.rot) {
+    if (!skinny.empty())
+      if (hipError_t e = launch_skinny(skinny.data(), int(skinny.size()), ydtype, ls)) return from_hip(e);
+    if (!gemms.empty())
+      if (hipError_t e = launch_gemm_group(gemms.data(), int(gemms.size()), ydtype, ls)) return from_hip(e);
+    // the longer calls one at a time, a rotated call's transform right before its linear, whose
+    // x' is then still in the caches
+    for (int i = 0; i < count; ++i) {
+      if (done[i] || lane[i] != ln) continue;
+      const paro_linear_args& c = calls[i];
+      if (!c.rot) {
+        if (paro_status s = run_linear(c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
+                                       static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
+                                       c.y, ydtype, slice[i], linear_ws_bytes(c.M, c.D, c.N), ls))
+          return s;
+        continue;
+      }
       const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
-      g.x = reinterpret_cast<const uint16_t*>(slice[i]);
-      g.x_nibble_order = true;
-      g.ws = slice[i] + xr_bytes;
-      g.ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
-    }
-    gemms.push_back(g);
-    done[i] = 1;
-  }
-  if (!skinny.empty())
-    if (hipError_t e = launch_skinny(skinny.data(), int(skinny.size()), ydtype, st)) return from_hip(e);
-  if (!gemms.empty())
-    if (hipError_t e = launch_gemm_group(gemms.data(), int(gemms.size()), ydtype, st)) return from_hip(e);
-  // the longer calls one at a time, a rotated call's transform right before its linear, whose
-  // x' is then still in the caches
-  for (int i = 0; i < count; ++i) {
-    if (done[i]) continue;
-    const paro_linear_args& c = calls[i];
-    if (!c.rot) {
-      if (paro_status s = run_linear(c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
+      const size_t part = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+      rots[i] = dev_rot(*c.rot);
+      if (hipError_t e = launch_rotate(rots[i], c.M, static_cast<const uint16_t*>(c.x),
+                                       reinterpret_cast<uint16_t*>(slice[i]), true, ls))
+        return from_hip(e);
+      if (paro_status s = run_linear(c.M, c.D, c.N, reinterpret_cast<const uint16_t*>(slice[i]), true, c.qweight,
                                      static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
-                                     c.y, ydtype, slice[i], linear_ws_bytes(c.M, c.D, c.N), st))
+                                     c.y, ydtype, slice[i] + xr_bytes, part, ls))
         return s;
-      continue;
     }
-    const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
-    const size_t part = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
-    rots[i] = dev_rot(*c.rot);
-    if (hipError_t e = launch_rotate(rots[i], c.M, static_cast<const uint16_t*>(c.x),
-                                     reinterpret_cast<uint16_t*>(slice[i]), true, st))
-      return from_hip(e);
-    if (paro_status s = run_linear(c.M, c.D, c.N, reinterpret_cast<const uint16_t*>(slice[i]), true, c.qweight,
-                                   static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
-                                   c.y, ydtype, slice[i] + xr_bytes, part, st))
-      return s;
+    return PARO_OK;
+  };
+  if (n_side) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideLane* L = nullptr;
+    if (side_lane_locked(st, &L)) {
+      if (hipEventRecord(L->fork, st) != hipSuccess || hipStreamWaitEvent(L->side, L->fork, 0) != hipSuccess)
+        return PARO_EHIP;
+      if (paro_status e = run_lane(1, L->side)) return e;
+      if (paro_status e = run_lane(0, st)) return e;
+      if (hipEventRecord(L->join, L->side) != hipSuccess || hipStreamWaitEvent(st, L->join, 0) != hipSuccess)
+        return PARO_EHIP;
+      return PARO_OK;
+    }
+    std::fill(lane.begin(), lane.end(), 0);  // no side lane (first use inside a capture): one stream
   }
-  return PARO_OK;
+  return run_lane(0, st);
 }
 
 }  // extern "C"

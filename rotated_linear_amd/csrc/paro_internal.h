@@ -180,8 +180,9 @@ hipError_t launch_reduce_group(const ReduceCall* calls, int n, int ydtype, hipSt
 
 // ---- linears of 17..64 rows (skinny.hip) ----
 constexpr int kSkinnyMaxM = 64;
-// Reductions longer than this many 128-channel groups are split over workgroups, and so are those
-// of calls too narrow to give kSkinnyMinUnits workgroups (256 columns each) otherwise.
+// Reductions longer than this many 128-channel groups are split over workgroups (in chunks of
+// half as many), and so are those of calls too narrow to give kSkinnyMinUnits workgroups (256
+// columns each) otherwise.
 constexpr int kSkinnyMaxGroups = 32;
 constexpr int kSkinnyMinUnits = 16;
 // Calls one skinny launch carries in its kernel arguments.

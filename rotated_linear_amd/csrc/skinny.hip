@@ -27,8 +27,8 @@
 //    1024 + z); the group scale is applied in float32 by rescaling the accumulators by
 //    s[g-1] / s[g] before group g and by the last scale at the end (the accumulators hold the
 //    sums in units of the last nonzero scale; a zero scale masks its group's codes);
-//  * a long reduction (more than 32 groups), or a call too narrow for 16 workgroups, is split
-//    over workgroups; the float32 partial sums go to the workspace and the ordered split
+//  * a long reduction (more than 32 groups: in chunks of 16), or a call too narrow for 16
+//    workgroups, is split over workgroups; the float32 partial sums go to the workspace and the ordered split
 //    reduction adds them. The split depends on the call's shape only, so a call computes the
 //    same bits alone and in a batch.
 #include <string.h>
@@ -384,7 +384,10 @@ SkinnyPlan skinny_plan(int M, int D, int N) {
   SkinnyPlan p;
   const int G = D / PARO_GROUP;
   p.tiles = (N + kTileN - 1) / kTileN;
-  int S = (G + kSkinnyMaxGroups - 1) / kSkinnyMaxGroups;
+  // up to kSkinnyMaxGroups groups in one workgroup; a longer reduction goes in chunks of half that
+  // (a down-projection-sized call then takes half-length workgroups, which fill in behind the
+  // full-length ones of the calls that share its launch)
+  int S = G <= kSkinnyMaxGroups ? 1 : (G + kSkinnyMaxGroups / 2 - 1) / (kSkinnyMaxGroups / 2);
   // a narrow call still takes at least kSkinnyMinUnits workgroups (at least 4 groups each)
   while (long(p.tiles) * S < kSkinnyMinUnits && G / (S + 1) >= 4) ++S;
   p.gps = (G + S - 1) / S;
