@@ -24,8 +24,15 @@
  * Conventions shared by every call
  *   - Shapes: x is [M][D] row-major float16, W is [N][D] row-major float16,
  *     y = transform(x) . dequant(W')^T is [M][N] row-major.
- *   - Packed weights: qweight uint8 [N][D/2] (byte t of row n holds channel 2t
- *     in bits 0..3 and channel 2t+1 in bits 4..7); scales float16 [N][D/128];
+ *   - Packed weights: qweight is N*D/2 bytes of 4-bit codes, two per byte:
+ *     byte t of row n's packed row (t < D/2) holds channel 2t in bits 0..3
+ *     and channel 2t+1 in bits 4..7. The rows are stored in blocks of 16 (the
+ *     last block holds the N % 16 remaining rows, if any): block b starts at
+ *     byte 16*b*D/2 and stores its R_b = min(16, N - 16*b) rows group by group,
+ *     so byte t of row n = 16*b + r is at
+ *         16*b*D/2 + (t/64)*R_b*64 + r*64 + t%64
+ *     (with N % 16 == 0: an array [N/16][D/128][16][64]). The linears read one
+ *     group of 16 rows as one contiguous kilobyte. scales float16 [N][D/128];
  *     zeros float16 [N][D/128] holding integers 0..15. Dequantized weight:
  *     (q - z) * scale.
  *   - Quantizer (per row n, group g of 128 channels of the folded weights b,
@@ -136,7 +143,8 @@ paro_status paro_rotation_prepare(int K, int D, const int32_t* pairs_host, const
  * For each row of W (float16 [N][D]), in float64 with no fused multiply-add:
  * apply the K stages (stage 1 first, same expressions as the activation side),
  * multiply by s, then quantize each 128-channel group as stated at the top and
- * pack the codes. Writes qweight [N][D/2], scales [N][D/128], zeros [N][D/128].
+ * pack the codes. Writes qweight (N*D/2 bytes, the blocked row order stated at
+ * the top), scales [N][D/128], zeros [N][D/128].
  * The outputs are bit-identical to the stated float64 definition
  * ("weight transformations are folded and quantized", section "A rotation
  * small enough to execute"; "real INT4 packing", section "From fake

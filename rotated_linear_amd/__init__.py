@@ -252,6 +252,8 @@ def paro_rotation_prepare(pairs, theta, scale, device="cuda") -> Rotation:
 
 def paro_pack_weights(rot: Rotation, W, out=None):
     """W float16 [N][D] on the GPU -> (qweight uint8 [N][D/2], scales f16 [N][D/128], zeros f16 [N][D/128]).
+    qweight's shape fixes its size only: its N*D/2 bytes hold the rows in blocks of 16, each
+    block group by group (include/paro.h, "Packed weights"), so ``qweight[n]`` is not row n.
     ``out``: an optional (qweight, scales, zeros) tuple of tensors of those shapes to write."""
     torch = _torch()
     N, D = int(W.shape[0]), rot.D

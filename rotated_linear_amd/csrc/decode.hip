@@ -293,7 +293,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
     int n = row0 + j * (NQ * 16);
     n = n < N ? n : N - 1;
     g = g < G ? g : G - 1;
-    w = ld16(qw + (__umul24(uint32_t(n), rowb) + uint32_t(g) * 64u + uint32_t(h) * 16u));
+    // blocked qweight layout (paro_internal.h): 16 rows x 64 bytes of a group are contiguous
+    const uint32_t un = uint32_t(n);
+    w = ld16(qw + (__umul24(un & ~15u, rowb) + (un & 15u) * 64u + uint32_t(g) * qw_group_stride(un, uint32_t(N)) +
+                   uint32_t(h) * 16u));
     const uint32_t gi = __umul24(uint32_t(n), uint32_t(G)) + uint32_t(g);
     sw = sc32[gi >> 1];
     zw = zr32[gi >> 1];

@@ -158,11 +158,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int b) {
     const int e = tid + i * kThreads, r = e >> 3, c = e & 7;
     a_off[i] = uint32_t(min(m0 + r, M - 1)) * uint32_t(D) * 2u + uint32_t(c) * 16u;
   }
-  uint32_t b_off[T::B_LD];
+  // packed weights in the blocked layout (paro_internal.h): a row's groups are b_gs[i] bytes apart
+  uint32_t b_off[T::B_LD], b_gs[T::B_LD];
 #pragma unroll
   for (int i = 0; i < T::B_LD; ++i) {
     const int e = min(tid + i * kThreads, BN * 2 - 1), r = e >> 1, c = e & 1;
-    b_off[i] = uint32_t(min(n0 + r, N - 1)) * uint32_t(D / 2) + uint32_t(c) * 16u;
+    const uint32_t n = uint32_t(min(n0 + r, N - 1));
+    b_off[i] = qw_row_offset(n, uint32_t(D)) + uint32_t(c) * 16u;
+    b_gs[i] = qw_group_stride(n, uint32_t(N));
   }
   const uint32_t sz_off = uint32_t(min(n0 + min(tid, BN - 1), N - 1)) * uint32_t(G) * 2u;
 
@@ -170,11 +173,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int b) {
     j = min(j, ns - 1);  // past the range: reload the last stage (unused)
     const int g = g_begin + (j >> 1), half = j & 1;
     const uint32_t ka = uint32_t(g) * 256u + uint32_t(half) * 128u;  // A bytes into the row
-    const uint32_t kb = uint32_t(g) * 64u + uint32_t(half) * 32u;    // packed B bytes into the row
+    const uint32_t kb = uint32_t(half) * 32u;                        // packed B bytes into the group
 #pragma unroll
     for (int i = 0; i < T::A_LD; ++i) s.a[i] = ld16(p.x, a_off[i] + ka);
 #pragma unroll
-    for (int i = 0; i < T::B_LD; ++i) s.b[i] = ld16(p.qw, b_off[i] + kb);
+    for (int i = 0; i < T::B_LD; ++i) s.b[i] = ld16(p.qw, b_off[i] + uint32_t(g) * b_gs[i] + kb);
     s.s = *reinterpret_cast<gptr<const uint16_t>>(reinterpret_cast<uintptr_t>(p.sc) + sz_off + uint32_t(g) * 2u);
     s.z = *reinterpret_cast<gptr<const uint16_t>>(reinterpret_cast<uintptr_t>(p.zr) + sz_off + uint32_t(g) * 2u);
   };

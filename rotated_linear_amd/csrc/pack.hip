@@ -61,7 +61,7 @@ __device__ inline double f16_bits_to_f64(uint16_t h) {
   return static_cast<double>(static_cast<float>(__builtin_bit_cast(_Float16, h)));
 }
 
-__global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(int D, int K, const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(int N, int D, int K, const uint16_t* __restrict__ W,
                                                                   const PairRec* __restrict__ recs,
                                                                   const float* __restrict__ s,
                                                                   uint8_t* __restrict__ qweight,
@@ -92,6 +92,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(int D, int K, c
 
   const int lane = tid & 63, wave = tid >> 6;
   const int G = D / PARO_GROUP;
+  // the row's group 0 and group stride in the blocked qweight layout (paro_internal.h)
+  uint8_t* const qrow = qweight + qw_row_offset<size_t>(size_t(n), size_t(D));
+  const size_t qstride = qw_group_stride<size_t>(size_t(n), size_t(N));
   for (int g = wave; g < G; g += kPackThreads / 64) {
     const double v0 = brow[g * PARO_GROUP + 2 * lane];
     const double v1 = brow[g * PARO_GROUP + 2 * lane + 1];
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(int D, int K, c
     double q1 = __builtin_rint(v1 / sc) + z;
     q0 = q0 < 0.0 ? 0.0 : (q0 > 15.0 ? 15.0 : q0);
     q1 = q1 < 0.0 ? 0.0 : (q1 > 15.0 ? 15.0 : q1);
-    qweight[size_t(n) * (D / 2) + g * 64 + lane] = uint8_t(int(q0) | (int(q1) << 4));
+    qrow[size_t(g) * qstride + lane] = uint8_t(int(q0) | (int(q1) << 4));
     if (lane == 0) {
       scales[size_t(n) * G + g] = s16;
       zeros[size_t(n) * G + g] = f64_to_f16_bits(z);
@@ -132,7 +135,7 @@ hipError_t launch_pack(const DevRot& R, int N, const uint16_t* W, uint8_t* qweig
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pack_rows_kernel, dim3(N), dim3(kPackThreads), lds, st, R.D, R.K, W, R.rec, R.s,
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(N), dim3(kPackThreads), lds, st, N, R.D, R.K, W, R.rec, R.s,
                      qweight, scales, zeros);
   return hipGetLastError();
 }

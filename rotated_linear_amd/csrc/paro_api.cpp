@@ -84,9 +84,11 @@ bool ws_overlaps(const void* ws, size_t need, int M, int D, int N, const void* x
 // it; never during a stream capture (the batch then runs on the caller's stream alone, computing
 // the same bits). g_side_mu is held from the fork to the join, so two host threads never
 // interleave one device's events.
+constexpr int kSideEvents = 16;
 struct SideLane {
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t ready[kSideEvents] = {};  // transforms run ahead on the side lane: one per transform
   bool ok = false;
 };
 constexpr int kMaxDevices = 64;
@@ -101,9 +103,15 @@ bool side_lane_locked(hipStream_t st, SideLane** out) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
     if (hipStreamCreateWithFlags(&L.side, hipStreamNonBlocking) != hipSuccess) return false;
-    if (hipEventCreateWithFlags(&L.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&L.join, hipEventDisableTiming) != hipSuccess) {
-      if (L.fork) (void)hipEventDestroy(L.fork);
+    bool made = hipEventCreateWithFlags(&L.fork, hipEventDisableTiming) == hipSuccess &&
+                hipEventCreateWithFlags(&L.join, hipEventDisableTiming) == hipSuccess;
+    for (int k = 0; made && k < kSideEvents; ++k)
+      made = hipEventCreateWithFlags(&L.ready[k], hipEventDisableTiming) == hipSuccess;
+    if (!made) {
+      for (hipEvent_t e : {L.fork, L.join})
+        if (e) (void)hipEventDestroy(e);
+      for (hipEvent_t e : L.ready)
+        if (e) (void)hipEventDestroy(e);
       (void)hipStreamDestroy(L.side);
       L = SideLane{};
       return false;
@@ -434,10 +442,10 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     slice[i] = wsp;
     wsp += c.rot ? rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) : linear_ws_bytes(c.M, c.D, c.N);
   }
-  // Two lanes: when the rotated calls still to run have several D, the calls of every D but the
-  // one with the most packed weight bytes (transforms and linears) run on the side lane,
-  // concurrently with the rest. Each call's kernels, tiling and summation order are the same in
-  // either lane, so the results do not depend on the split.
+  // Two lanes: when the rotated calls still to run have several D, the transforms of every D but
+  // the one with the most packed weight bytes (lane 1) run on the side lane, concurrently with
+  // the rest. Each call's kernels, tiling and summation order do not depend on the lane or the
+  // order, so neither do the results.
   std::vector<char> lane(size_t(count > 0 ? count : 0), 0);
   int n_side = 0;
   {
@@ -464,7 +472,10 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
     }
   }
   std::vector<char> rotated(size_t(count > 0 ? count : 0), 0);
-  auto run_lane = [&](int ln, hipStream_t ls) -> paro_status {
+  // The transforms of lane ln's rotated calls that have not run: the calls of up to
+  // kBatchTransformMaxM rows as one batched launch per D, and with long_too the longer calls, one
+  // launch each.
+  auto transforms = [&](int ln, hipStream_t ls, bool long_too) -> paro_status {
     for (int i = 0; i < count; ++i) {
       if (done[i] || lane[i] != ln || !calls[i].rot || rotated[i] || calls[i].M > kBatchTransformMaxM) continue;
       std::vector<RotateJob> jobs;
@@ -477,8 +488,37 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
       }
       if (hipError_t e = launch_rotate_batch(jobs.data(), int(jobs.size()), true, ls)) return from_hip(e);
     }
-    // decode-shaped linears whose transform just ran in a batch (D or K beyond what the decode
-    // kernel runs inside): one decode launch per D on the transformed x, as for the plain calls
+    if (long_too)
+      for (int i = 0; i < count; ++i) {
+        if (done[i] || lane[i] != ln || !calls[i].rot || rotated[i]) continue;
+        rots[i] = dev_rot(*calls[i].rot);
+        if (hipError_t e = launch_rotate(rots[i], calls[i].M, static_cast<const uint16_t*>(calls[i].x),
+                                         reinterpret_cast<uint16_t*>(slice[i]), true, ls))
+          return from_hip(e);
+        rotated[i] = 1;
+      }
+    return PARO_OK;
+  };
+  // One linear on x, or on its transformed x in the call's slice.
+  auto linear_of = [&](int i, hipStream_t ls) -> paro_status {
+    const paro_linear_args& c = calls[i];
+    if (!c.rot)
+      return run_linear(c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
+                        static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, ydtype,
+                        slice[i], linear_ws_bytes(c.M, c.D, c.N), ls);
+    const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
+    return run_linear(c.M, c.D, c.N, reinterpret_cast<const uint16_t*>(slice[i]), true, c.qweight,
+                      static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, ydtype,
+                      slice[i] + xr_bytes, rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes, ls);
+  };
+  // The linears of lane ln (a rotated call's transform has run), the skinny launches' split
+  // reductions appended to `reduces`. With long_calls, then the calls of more than
+  // kBatchTransformMaxM rows one at a time; a rotated one whose transform has not run gets it
+  // right before its linear, whose x' is then still in the caches.
+  std::vector<ReduceCall> reduces;
+  auto linears = [&](int ln, hipStream_t ls, bool long_calls) -> paro_status {
+    // decode-shaped linears on an already transformed x (D or K beyond what the decode kernel
+    // runs inside): one decode launch per D, as for the plain calls
     for (int i = 0; i < count; ++i) {
       if (done[i] || lane[i] != ln || !rotated[i] || !decode_takes(-1, calls[i].M, calls[i].D, calls[i].N)) continue;
       std::vector<DecodeCall> group;
@@ -492,86 +532,111 @@ paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydty
       }
       if (hipError_t e = launch_decode(calls[i].D, ydtype, group.data(), int(group.size()), ls)) return from_hip(e);
     }
-    // GEMM-shaped linears of up to 256 rows, on x or on an already transformed x: the calls
-    // sharing a tiling run in one launch, their split reductions in one more (one such call
-    // rarely fills the GPU; larger ones do, and run one at a time below)
+    // GEMM-shaped linears of up to kBatchTransformMaxM rows: the 17..64-row calls in one skinny
+    // launch, the others as grouped GEMM launches (one per tiling) with their split reductions
+    // (one such call rarely fills the GPU; larger ones do, and run one at a time below)
     std::vector<GemmCall> gemms;
     std::vector<SkinnyJob> skinny;
     for (int i = 0; i < count; ++i) {
       if (done[i] || lane[i] != ln || (calls[i].rot && !rotated[i]) || calls[i].M > kBatchTransformMaxM) continue;
       const paro_linear_args& c = calls[i];
-      if (skinny_takes(c.M, c.D, c.N)) {  // 17..64 rows: one skinny launch for all of them
-        SkinnyJob j{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
-                    static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
-                    linear_ws_bytes(c.M, c.D, c.N)};
-        if (c.rot) {
-          const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
-          j.x = reinterpret_cast<const uint16_t*>(slice[i]);
-          j.x_nibble_order = true;
-          j.ws = slice[i] + xr_bytes;
-          j.ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
-        }
-        skinny.push_back(j);
-        done[i] = 1;
-        continue;
-      }
-      GemmCall g{c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
-                 static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros), c.y, slice[i],
-                 linear_ws_bytes(c.M, c.D, c.N)};
+      const uint16_t* x = static_cast<const uint16_t*>(c.x);
+      void* ws = slice[i];
+      size_t ws_bytes = linear_ws_bytes(c.M, c.D, c.N);
       if (c.rot) {
         const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
-        g.x = reinterpret_cast<const uint16_t*>(slice[i]);
-        g.x_nibble_order = true;
-        g.ws = slice[i] + xr_bytes;
-        g.ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
+        x = reinterpret_cast<const uint16_t*>(slice[i]);
+        ws = slice[i] + xr_bytes;
+        ws_bytes = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
       }
-      gemms.push_back(g);
+      if (skinny_takes(c.M, c.D, c.N))
+        skinny.push_back(SkinnyJob{c.M, c.D, c.N, x, c.rot != nullptr, c.qweight, static_cast<const uint16_t*>(c.scales),
+                                   static_cast<const uint16_t*>(c.zeros), c.y, ws, ws_bytes});
+      else
+        gemms.push_back(GemmCall{c.M, c.D, c.N, x, c.rot != nullptr, c.qweight, static_cast<const uint16_t*>(c.scales),
+                                 static_cast<const uint16_t*>(c.zeros), c.y, ws, ws_bytes});
       done[i] = 1;
     }
     if (!skinny.empty())
-      if (hipError_t e = launch_skinny(skinny.data(), int(skinny.size()), ydtype, ls)) return from_hip(e);
+      if (hipError_t e = launch_skinny(skinny.data(), int(skinny.size()), ydtype, ls, &reduces)) return from_hip(e);
     if (!gemms.empty())
       if (hipError_t e = launch_gemm_group(gemms.data(), int(gemms.size()), ydtype, ls)) return from_hip(e);
-    // the longer calls one at a time, a rotated call's transform right before its linear, whose
-    // x' is then still in the caches
+    if (!long_calls) return PARO_OK;
     for (int i = 0; i < count; ++i) {
       if (done[i] || lane[i] != ln) continue;
-      const paro_linear_args& c = calls[i];
-      if (!c.rot) {
-        if (paro_status s = run_linear(c.M, c.D, c.N, static_cast<const uint16_t*>(c.x), false, c.qweight,
-                                       static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
-                                       c.y, ydtype, slice[i], linear_ws_bytes(c.M, c.D, c.N), ls))
-          return s;
-        continue;
+      if (calls[i].rot && !rotated[i]) {
+        rots[i] = dev_rot(*calls[i].rot);
+        if (hipError_t e = launch_rotate(rots[i], calls[i].M, static_cast<const uint16_t*>(calls[i].x),
+                                         reinterpret_cast<uint16_t*>(slice[i]), true, ls))
+          return from_hip(e);
+        rotated[i] = 1;
       }
-      const size_t xr_bytes = align256(size_t(c.M) * size_t(c.D) * 2);
-      const size_t part = rotated_ws_bytes(c.rot->K, c.M, c.D, c.N) - xr_bytes;
-      rots[i] = dev_rot(*c.rot);
-      if (hipError_t e = launch_rotate(rots[i], c.M, static_cast<const uint16_t*>(c.x),
-                                       reinterpret_cast<uint16_t*>(slice[i]), true, ls))
-        return from_hip(e);
-      if (paro_status s = run_linear(c.M, c.D, c.N, reinterpret_cast<const uint16_t*>(slice[i]), true, c.qweight,
-                                     static_cast<const uint16_t*>(c.scales), static_cast<const uint16_t*>(c.zeros),
-                                     c.y, ydtype, slice[i] + xr_bytes, part, ls))
-        return s;
+      if (paro_status s = linear_of(i, ls)) return s;
+      done[i] = 1;
     }
     return PARO_OK;
   };
-  if (n_side) {
+  auto finish = [&](hipStream_t ls) -> paro_status {
+    if (reduces.empty()) return PARO_OK;
+    return from_hip(launch_reduce_group(reduces.data(), int(reduces.size()), ydtype, ls));
+  };
+
+  // Several long rotated calls (prefill-shaped): their transforms run ahead, one after another, on
+  // the side lane, each followed by a ready event; the caller's stream runs everything else and
+  // then the long linears in order, each waiting only for its own transform.
+  std::vector<int> longs;
+  for (int i = 0; i < count; ++i)
+    if (!done[i] && calls[i].M > kBatchTransformMaxM && calls[i].rot) longs.push_back(i);
+  if (longs.size() >= 2 || n_side) {
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideLane* L = nullptr;
     if (side_lane_locked(st, &L)) {
       if (hipEventRecord(L->fork, st) != hipSuccess || hipStreamWaitEvent(L->side, L->fork, 0) != hipSuccess)
         return PARO_EHIP;
-      if (paro_status e = run_lane(1, L->side)) return e;
-      if (paro_status e = run_lane(0, st)) return e;
-      if (hipEventRecord(L->join, L->side) != hipSuccess || hipStreamWaitEvent(st, L->join, 0) != hipSuccess)
-        return PARO_EHIP;
-      return PARO_OK;
+      if (longs.size() >= 2) {
+        std::fill(lane.begin(), lane.end(), 0);
+        for (size_t k = 0; k < longs.size(); ++k) {
+          const int i = longs[k];
+          rots[i] = dev_rot(*calls[i].rot);
+          if (hipError_t e = launch_rotate(rots[i], calls[i].M, static_cast<const uint16_t*>(calls[i].x),
+                                           reinterpret_cast<uint16_t*>(slice[i]), true, L->side))
+            return from_hip(e);
+          // an event is reused after kSideEvents transforms: a later linear then waits for a
+          // later transform too (still in order, only less overlap)
+          if (hipEventRecord(L->ready[k % kSideEvents], L->side) != hipSuccess) return PARO_EHIP;
+          rotated[i] = 1;
+        }
+        if (hipEventRecord(L->join, L->side) != hipSuccess) return PARO_EHIP;
+        if (paro_status e = transforms(0, st, false)) return e;
+        if (paro_status e = linears(0, st, false)) return e;
+        size_t k = 0;
+        for (int i = 0; i < count; ++i) {
+          if (done[i]) continue;
+          if (calls[i].rot && hipStreamWaitEvent(st, L->ready[k++ % kSideEvents], 0) != hipSuccess) return PARO_EHIP;
+          if (paro_status s = linear_of(i, st)) return s;
+          done[i] = 1;
+        }
+      } else {
+        // Two lanes by D: the side lane runs the transforms of every D but the one with the most
+        // packed weight bytes while the caller's stream runs that D's; then all the linears run on
+        // the caller's stream, as few launches as for one D (one skinny launch fills the GPU
+        // better than two that follow each other).
+        if (paro_status e = transforms(1, L->side, true)) return e;
+        if (hipEventRecord(L->join, L->side) != hipSuccess) return PARO_EHIP;
+        if (paro_status e = transforms(0, st, false)) return e;
+        if (hipStreamWaitEvent(st, L->join, 0) != hipSuccess) return PARO_EHIP;
+        std::fill(lane.begin(), lane.end(), 0);
+        if (paro_status e = linears(0, st, true)) return e;
+      }
+      if (hipStreamWaitEvent(st, L->join, 0) != hipSuccess) return PARO_EHIP;
+      return finish(st);
     }
-    std::fill(lane.begin(), lane.end(), 0);  // no side lane (first use inside a capture): one stream
   }
-  return run_lane(0, st);
+  // one stream (no side lane: its first use would fall inside a stream capture)
+  std::fill(lane.begin(), lane.end(), 0);
+  if (paro_status e = transforms(0, st, false)) return e;
+  if (paro_status e = linears(0, st, true)) return e;
+  return finish(st);
 }
 
 }  // extern "C"

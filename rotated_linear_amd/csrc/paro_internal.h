@@ -13,6 +13,24 @@ namespace paro {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// ---- packed weight layout (qweight, include/paro.h) ----
+// Rows in blocks of 16 (the last block holds the N % 16 remaining rows, if any); block b starts at
+// byte 16 b D/2 and holds its R_b rows group by group: the 64 bytes of group g of the block's row
+// r sit at 16 b D/2 + g R_b 64 + r 64. A wave's 16 rows x 64 bytes of one group are then one
+// contiguous kilobyte (row-major rows put them 64 bytes each, D/2 bytes apart).
+constexpr int kQwBlockRows = 16;
+// Byte offset of group 0 of row n, and the bytes from one group of row n to the next (T: a 32-bit
+// type where the caller has checked that N D/2 fits, else a 64-bit one).
+template <class T>
+__host__ __device__ inline T qw_row_offset(T n, T D) {
+  return (n & ~T(kQwBlockRows - 1)) * (D / 2) + (n & T(kQwBlockRows - 1)) * 64;
+}
+template <class T>
+__host__ __device__ inline T qw_group_stride(T n, T N) {
+  const T n0 = n & ~T(kQwBlockRows - 1);
+  return (N - n0 < T(kQwBlockRows) ? N - n0 : T(kQwBlockRows)) * 64;
+}
+
 // Device descriptor of a prepared transform. Three sections, each 256-byte aligned:
 //   rec    PairRec [K][D/2]  {i | (j << 16), cos, sin} (12 bytes: one 3-dword load per pair)
 //   inv_s  float   [D]       1/s rounded once to float32 (activation side)
@@ -207,8 +225,10 @@ struct SkinnyJob {
   size_t ws_bytes;
 };
 // The calls sharing x's word order run as one launch (up to kSkinnyMaxCalls each), their split
-// reductions as one more.
-hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t st);
+// reductions as one more; with `defer` the reductions are appended there instead, for the caller
+// to launch (launch_reduce_group) after later work on the same stream.
+hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t st,
+                         std::vector<ReduceCall>* defer = nullptr);
 
 // ---- the fixed scratch buffer of paro_rotated_linear_noalloc (noalloc.hip) ----
 constexpr size_t kScratchBytes = size_t(64) << 20;

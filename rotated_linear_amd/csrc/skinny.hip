@@ -13,10 +13,9 @@
 //    256-column tile over a range of 128-channel groups; each of its 4 column waves owns 64 of the
 //    columns (four 16-column tiles), so every weight is loaded and dequantized exactly once;
 //  * the packed weights go from HBM straight into registers (no LDS, no barrier on their path):
-//    per group and tile a wave-wide load reads 16 weight rows x 64 contiguous bytes (the group),
-//    L groups ahead of their use, in a register ring whose slots are compile-time indices, so
-//    the compiler's wait counts stay exact; the two K-waves read adjacent groups, so together
-//    they take whole 128-byte lines;
+//    per group and tile a wave-wide load reads 16 weight rows x 64 bytes (the group), one
+//    contiguous kilobyte in the blocked weight layout, L groups ahead of their use, in a register
+//    ring whose slots are compile-time indices, so the compiler's wait counts stay exact;
 //  * the activations (x, or the transformed x, float16) are staged through LDS, one group per
 //    K-wave at a time in a two-slot ring, loaded L groups ahead together with the weights of the
 //    same group (loads complete in issue order, so waiting for a group's activations never waits
@@ -162,11 +161,14 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
     a_lds[c] = uint32_t(qs) * kGroupBytes + uint32_t(row) * (kLdaH * 2) + uint32_t(c16) * 16u;
   }
   // ---- weights: this lane's column in each of the wave's four 16-column tiles, chunk q
-  uint32_t b_off[4];
+  // (blocked layout, paro_internal.h: a wave-wide load of a tile's group is one contiguous
+  // kilobyte; a row's groups are b_gs[tn] bytes apart)
+  uint32_t b_off[4], b_gs[4];
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn) {
-    const int n = min(n_wave + 16 * tn + r16, N - 1);  // columns past N repeat the last (never stored)
-    b_off[tn] = uint32_t(n) * uint32_t(D / 2) + uint32_t(q) * 16u;
+    const uint32_t n = uint32_t(min(n_wave + 16 * tn + r16, N - 1));  // columns past N repeat the last (never stored)
+    b_off[tn] = qw_row_offset(n, uint32_t(D)) + uint32_t(q) * 16u;
+    b_gs[tn] = qw_group_stride(n, uint32_t(N));
   }
   // ---- group scales and zeros: thread u owns column u of the tile for K-wave qs. It loads the
   // column's scale and zero of each group that K-wave takes, keeps the chain of the K-wave's
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
     for (int c = 0; c < AC; ++c) areg[slot_i][c] = ldg16(C.x, a_off[c] + uint32_t(ga) * 256u);
     const int gb = min(g0 + WK * i + wk, g1 - 1);
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) breg[slot_i][tn] = ldg16(C.qw, b_off[tn] + uint32_t(gb) * 64u);
+    for (int tn = 0; tn < 4; ++tn) breg[slot_i][tn] = ldg16(C.qw, b_off[tn] + uint32_t(gb) * b_gs[tn]);
     if constexpr (!SZB) {
       sreg[slot_i] = ldg_u16(C.sc, szc_off + uint32_t(ga) * 2u);
       zreg[slot_i] = ldg_u16(C.zr, szc_off + uint32_t(ga) * 2u);
@@ -408,8 +410,9 @@ bool skinny_takes(int M, int D, int N) {
   return size_t(M) * size_t(D) * 2 < (size_t(1) << 31) && size_t(N) * size_t(D / 2) < (size_t(1) << 31);
 }
 
-hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t st) {
-  std::vector<ReduceCall> reduces;
+hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t st, std::vector<ReduceCall>* defer) {
+  std::vector<ReduceCall> own;
+  std::vector<ReduceCall>& reduces = defer ? *defer : own;
   for (int variant = 0; variant < 4; ++variant) {
     const int x_perm = variant & 1, szb = variant >> 1;
     int i = 0;
@@ -453,7 +456,7 @@ hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t s
       if (e != hipSuccess) return e;
     }
   }
-  if (reduces.empty()) return hipSuccess;
+  if (defer || reduces.empty()) return hipSuccess;
   return launch_reduce_group(reduces.data(), int(reduces.size()), ydtype, st);
 }
 

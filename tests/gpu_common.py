@@ -27,6 +27,44 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
+# The library's packed-weight layout, written out from its definition in include/paro.h: rows in
+# blocks of 16 (the last block holds the N % 16 remaining rows), block b starting at byte
+# 16 b D/2 and holding group g (64 bytes per row) of its R_b rows contiguously, row r of the block
+# at byte 16 b D/2 + g R_b 64 + r 64. The oracle packs row-major [N][D/2]; these move between the
+# two (the bytes are the same, only their order differs).
+def to_blocked(q: np.ndarray) -> np.ndarray:
+    q = np.asarray(q, np.uint8)
+    N, H = q.shape
+    out = np.empty(N * H, np.uint8)
+    for b0 in range(0, N, 16):
+        R = min(16, N - b0)
+        out[b0 * H:(b0 + R) * H] = q[b0:b0 + R].reshape(R, H // 64, 64).transpose(1, 0, 2).reshape(-1)
+    return out.reshape(N, H)
+
+
+def from_blocked(qb: np.ndarray) -> np.ndarray:
+    qb = np.asarray(qb, np.uint8)
+    N, H = qb.shape
+    flat = qb.reshape(-1)
+    out = np.empty((N, H), np.uint8)
+    for b0 in range(0, N, 16):
+        R = min(16, N - b0)
+        out[b0:b0 + R] = flat[b0 * H:(b0 + R) * H].reshape(H // 64, R, 64).transpose(1, 0, 2).reshape(R, H)
+    return out
+
+
+def dev_weights(w, torch):
+    """Oracle-packed (row-major qweight, scales, zeros) -> the library's device operands."""
+    qw, sc, z = w
+    return dev(to_blocked(qw), torch), dev(sc, torch), dev(z, torch)
+
+
+def host_weights(w):
+    """The library's device (qweight, scales, zeros) -> host arrays with a row-major qweight."""
+    qw, sc, z = w
+    return from_blocked(host(qw)), host(sc), host(z)
+
+
 @functools.lru_cache(maxsize=None)
 def linear_inputs(wid: int, index: int):
     return W.make_linear(wid, index)

@@ -51,7 +51,7 @@ def test_pack_bitexact(wid, index):
     rows = C.sample_rows(L.spec.N, 384, seed=wid * 10 + index)
     key = None if len(rows) == L.spec.N else tuple(int(r) for r in rows)
     oq, osc, oz = C.oracle_pack_rows(wid, index, key)
-    gq, gsc, gz = C.host(qw)[rows], C.host(sc)[rows], C.host(z)[rows]
+    gq, gsc, gz = (t[rows] for t in C.host_weights((qw, sc, z)))
     assert np.array_equal(gq, oq), f"qweight differs in {(gq != oq).sum()} bytes"
     assert np.array_equal(gsc.view(np.uint16), osc.view(np.uint16)), "scales differ"
     assert np.array_equal(gz.astype(np.float64), oz.astype(np.float64)), "zeros differ"
@@ -83,7 +83,8 @@ def test_pack_edge_shapes():
         C.log(f"pack edge D={D} N={N} K={K}")
         qw, sc, z = rl.paro_pack_weights(_rot(L), C.dev(L.W, torch))
         oq, osc, oz = O.pack_weights(L.W, L.pairs, L.theta, L.scale)
-        assert np.array_equal(C.host(qw), oq)
+        assert np.array_equal(C.from_blocked(C.host(qw)), oq)
+        assert np.array_equal(C.host(qw), C.to_blocked(oq))
         assert np.array_equal(C.host(sc).view(np.uint16), osc.view(np.uint16))
         assert np.array_equal(C.host(z).astype(np.float64), oz.astype(np.float64))
 
@@ -212,10 +213,10 @@ def test_linear_parity(wid, index, M):
     key = None if len(rows_w) == N else tuple(int(r) for r in rows_w)
     oracle_pack = C.oracle_pack_rows(wid, index, key)
     if key is None:
-        gpu_w = tuple(C.dev(t, torch) for t in oracle_pack)  # the oracle's own packed weights
+        gpu_w = C.dev_weights(oracle_pack, torch)  # the oracle's own packed weights
     else:
         gpu_w = rl.paro_pack_weights(_rot(L), C.dev(L.W, torch))  # full weights; sampled rows checked bit-exact
-        assert np.array_equal(C.host(gpu_w[0])[rows_w], oracle_pack[0])
+        assert np.array_equal(C.from_blocked(C.host(gpu_w[0]))[rows_w], oracle_pack[0])
     if M > 512:  # token-row sample for the large prefill batches
         Lm = L
         x_rows = C.sample_rows(M, 96, seed=M + index)
@@ -254,7 +255,7 @@ def test_linear_edge_shapes(M, D, N, K):
     L = W.custom_linear(21, M, D, N, K)
     C.log(f"linear edge M={M} D={D} N={N} K={K}")
     op = O.pack_weights(L.W, L.pairs, L.theta, L.scale)
-    _linear_case(L, M, np.arange(N), op, tuple(C.dev(t, torch) for t in op), configured=False)
+    _linear_case(L, M, np.arange(N), op, C.dev_weights(op, torch), configured=False)
 
 
 @pytest.mark.parametrize("M", [1, 3, 4, 16, 200])
@@ -285,7 +286,7 @@ def test_inside_and_separate_transform_agree():
         a = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z, out_dtype=dt))
         b = C.host(rl.paro_rotated_linear(rot, xd[:4].contiguous(), qw, sc, z, out_dtype=dt))
         assert np.array_equal(a[:4].view(np.uint8), b.view(np.uint8))
-    deq = O.dequantize(*(C.host(t) for t in (qw, sc, z)))
+    deq = O.dequantize(*C.host_weights((qw, sc, z)))
     ref = O.f16_rne(O.transform_activations(L.x, L.pairs, L.theta, L.scale)).astype(np.float64) @ deq.T
     mx, rel = C.linear_metrics(a, ref)
     assert mx <= C.MAX_ABS and rel <= C.REL_L2, (mx, rel)
@@ -298,7 +299,7 @@ def test_split_reduction_and_fallback():
     L = W.custom_linear(43, 64, 4096, 600, 2)
     C.log("split / unsplit reduction M=64 D=4096 N=600")
     op = O.pack_weights(L.W, L.pairs, L.theta, L.scale)
-    qw, sc, z = (C.dev(t, torch) for t in op)
+    qw, sc, z = C.dev_weights(op, torch)
     xd = C.dev(L.x, torch)
     need = rl.paro_workspace_bytes(64, 4096, 600)
     ref = L.x.astype(np.float64) @ O.dequantize(*op).T
@@ -355,7 +356,7 @@ def _batch_inputs(specs):
         L = W.custom_linear(seed, M, D, N, 0 if K is None else K)
         rot = None if K is None else _rot(L)
         if rot is None:
-            qw, sc, z = (C.dev(t, torch) for t in O.pack_weights(L.W, L.pairs[:0], L.theta[:0], np.ones_like(L.scale)))
+            qw, sc, z = C.dev_weights(O.pack_weights(L.W, L.pairs[:0], L.theta[:0], np.ones_like(L.scale)), torch)
         else:
             qw, sc, z = rl.paro_pack_weights(rot, C.dev(L.W, torch))
         out.append((L, rot, C.dev(L.x, torch), (qw, sc, z)))
@@ -389,6 +390,13 @@ def _single(rot, xd, w, dt):
     # launches (one per tiling and x order) and one grouped split reduction
     [(500, 200, 1024, 2048, 8), (501, 20, 1024, 64, 8), (502, 250, 1024, 1536, None), (503, 17, 1024, 4096, None),
      (504, 128, 2048, 256, 4), (505, 64, 4096, 1024, 8), (506, 64, 4096, 1024, None)],
+    # long rotated calls (M > 256, prefill-shaped) whose transforms run ahead on the library's
+    # second stream while the linears run in order, each waiting for its own transform: 18 of
+    # them (more than the 16 ready events, which are then reused), two D, ragged M, plain long
+    # calls and short calls in between
+    [(600 + i, (257, 300, 513, 384)[i % 4], (512, 1024)[i % 2], 64 + 32 * (i % 3), (8, 2, 12)[i % 3])
+     for i in range(18)]
+    + [(630, 400, 512, 96, None), (631, 40, 1024, 128, 8), (632, 3, 512, 64, 8), (633, 300, 1024, 64, None)],
     # one layer of the 1.5B-shaped stack at decode M = 1 (q, k, v, o, gate, up, down), as the
     # whole-stack decode step batches it
     [(400 + i, 1, s.D, s.N, s.K) for i, s in enumerate(W.MODEL_LINEARS)],
@@ -405,7 +413,7 @@ def test_batch_matches_single_calls_bitwise(specs):
     # and against the oracle (the spec bar) for the float32 outputs
     ys = [C.host(y) for y in rl.paro_linear_batch(calls, out_dtype=torch.float32)]
     for (L, rot, xd, w), y in zip(ins, ys):
-        deq = O.dequantize(*(C.host(t) for t in w))
+        deq = O.dequantize(*C.host_weights(w))
         if rot is None:
             ref = L.x.astype(np.float64) @ deq.T
         else:
@@ -455,7 +463,7 @@ def test_workload_batch_as_benchmarked(wid, Ms):
         single = C.host(rl.paro_rotated_linear(rot, xd, *w, out_dtype=torch.float32))
         assert np.array_equal(y.view(np.uint8), single.view(np.uint8)), (L.spec.name, xd.shape[0])
         rows = C.sample_rows(L.spec.N, 256, seed=xd.shape[0])
-        deq = O.dequantize(*(C.host(t)[rows] for t in w))
+        deq = O.dequantize(*(t[rows] for t in C.host_weights(w)))
         a = O.transform_activations(L.x[:xd.shape[0]], L.pairs, L.theta, L.scale)
         ref = O.f16_rne(a).astype(np.float64) @ deq.T
         mx, rel = C.linear_metrics(y[:, rows], ref)

@@ -116,7 +116,7 @@ def test_crafted_pack_bitexact(kind):
     L = _inputs(kind)
     C.log(f"crafted pack kind={kind} K={L.spec.K} D={D} N={N}")
     rot = rl.paro_rotation_prepare(L.pairs, L.theta, L.scale)
-    qw, sc, z = (C.host(t) for t in rl.paro_pack_weights(rot, C.dev(L.W, torch)))
+    qw, sc, z = C.host_weights(rl.paro_pack_weights(rot, C.dev(L.W, torch)))
     oq, osc, oz = O.pack_weights(L.W, L.pairs, L.theta, L.scale)
     assert np.array_equal(qw, oq), f"qweight differs in {(qw != oq).sum()} bytes"
     assert np.array_equal(sc.view(np.uint16), osc.view(np.uint16)), "scales differ"
@@ -145,7 +145,7 @@ def test_crafted_linears(kind, M):
     rot = rl.paro_rotation_prepare(L.pairs, L.theta, L.scale)
     w = rl.paro_pack_weights(rot, C.dev(L.W, torch))
     oq, osc, oz = O.pack_weights(L.W, L.pairs, L.theta, L.scale)
-    assert np.array_equal(C.host(w[0]), oq)
+    assert np.array_equal(C.from_blocked(C.host(w[0])), oq)
     deq = O.dequantize(oq, osc, oz)
     x = L.x[:M]
     xd = C.dev(x, torch)
@@ -194,7 +194,7 @@ def test_zero_scales_contribute_nothing(M):
     deq = O.dequantize(oq, osc, oz)
     x = L.x[:M]
     xd = C.dev(x, torch)
-    w = tuple(C.dev(t, torch) for t in (oq, osc, oz))
+    w = C.dev_weights((oq, osc, oz), torch)
     ref = x.astype(np.float64) @ deq.T
     need = rl.paro_workspace_bytes(M, D, N)
     for ws in (torch.empty(max(need, 256), dtype=torch.uint8, device="cuda"),

@@ -34,7 +34,7 @@ def _check(L, rot, w, dt):
     ref_call = C.host(rl.paro_rotated_linear(rot, xd, *w, out_dtype=dt, ws=ws))
     assert np.array_equal(got.view(np.uint8), ref_call.view(np.uint8)), "differs from paro_rotated_linear"
     if dt == torch.float32:
-        deq = O.dequantize(*(C.host(t) for t in w))
+        deq = O.dequantize(*C.host_weights(w))
         a = O.transform_activations(L.x, L.pairs, L.theta, L.scale)
         mx, rel = C.linear_metrics(got, O.f16_rne(a).astype(np.float64) @ deq.T)
         assert mx <= C.MAX_ABS and rel <= C.REL_L2, (mx, rel)
