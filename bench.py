@@ -415,7 +415,8 @@ CALIB_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
 # was taken on
 TRAFFIC_FILES = {"decode": os.path.join(ROOT, "profiles", "traffic_layer8b_decode_M64.md"),
                  "prefill": os.path.join(ROOT, "profiles", "traffic_layer8b_prefill_M4096.md")}
-KERNEL_SOURCES = {"decode": ["rotated_linear_amd/csrc/gemm.hip", "rotated_linear_amd/csrc/paro_internal.h"],
+KERNEL_SOURCES = {"decode": ["rotated_linear_amd/csrc/skinny.hip", "rotated_linear_amd/csrc/gemm.hip",
+                             "rotated_linear_amd/csrc/paro_internal.h"],
                   "prefill": ["rotated_linear_amd/csrc/gemm.hip", "rotated_linear_amd/csrc/paro_internal.h"]}
 
 
