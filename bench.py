@@ -246,9 +246,12 @@ def cpu_baseline(step, seconds, rows=None):
 
     import oracle as O
 
+    import workloads as W
+
     deq = {}
     for li, lin in enumerate(step.linears):
         qw, sc, z = (t.cpu().numpy() for t in lin.w)
+        qw = W.qweight_from_blocked(qw)  # the library's blocked order -> the oracle's row-major one
         n = lin.N if rows is None else min(rows, lin.N)
         deq[li] = O.dequantize(qw[:n], sc[:n], z[:n])
     xs = {k: v.cpu().numpy() for k, v in step.x.items()}

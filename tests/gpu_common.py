@@ -27,30 +27,9 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-# The library's packed-weight layout, written out from its definition in include/paro.h: rows in
-# blocks of 16 (the last block holds the N % 16 remaining rows), block b starting at byte
-# 16 b D/2 and holding group g (64 bytes per row) of its R_b rows contiguously, row r of the block
-# at byte 16 b D/2 + g R_b 64 + r 64. The oracle packs row-major [N][D/2]; these move between the
-# two (the bytes are the same, only their order differs).
-def to_blocked(q: np.ndarray) -> np.ndarray:
-    q = np.asarray(q, np.uint8)
-    N, H = q.shape
-    out = np.empty(N * H, np.uint8)
-    for b0 in range(0, N, 16):
-        R = min(16, N - b0)
-        out[b0 * H:(b0 + R) * H] = q[b0:b0 + R].reshape(R, H // 64, 64).transpose(1, 0, 2).reshape(-1)
-    return out.reshape(N, H)
-
-
-def from_blocked(qb: np.ndarray) -> np.ndarray:
-    qb = np.asarray(qb, np.uint8)
-    N, H = qb.shape
-    flat = qb.reshape(-1)
-    out = np.empty((N, H), np.uint8)
-    for b0 in range(0, N, 16):
-        R = min(16, N - b0)
-        out[b0:b0 + R] = flat[b0 * H:(b0 + R) * H].reshape(H // 64, R, 64).transpose(1, 0, 2).reshape(R, H)
-    return out
+# the library's blocked qweight order <-> the oracle's row-major one (include/paro.h)
+to_blocked = W.qweight_to_blocked
+from_blocked = W.qweight_from_blocked
 
 
 def dev_weights(w, torch):
