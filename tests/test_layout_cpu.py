@@ -1,4 +1,5 @@
-"""The packed-weight layout helpers the GPU tests use to move between the oracle's row-major
+"""The packed-weight layout helpers (workloads.qweight_to_blocked / qweight_from_blocked) the GPU tests,
+smoke() and the CPU baseline use to move between the oracle's row-major
 qweight and the library's blocked one (include/paro.h, "Packed weights"): pinned here against
 the definition's byte formula, on ragged row counts."""
 from __future__ import annotations
