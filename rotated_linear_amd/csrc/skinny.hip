@@ -60,7 +60,10 @@ struct SkLds {
   static constexpr uint32_t kCst = WK * kGroupBytes;        // column records [WK][BN]
   static constexpr uint32_t kBuf = kCst + WK * kBN * 16;    // one buffer
   static constexpr uint32_t kFinal = 2 * kBuf;              // last scales [WK][BN] float, after the loop
-  static constexpr uint32_t kTotal = kFinal + WK * kBN * 4;
+  static constexpr uint32_t kTab = kFinal + WK * kBN * 4;    // TAB: scale table [32][BN] {scale, zero}
+  static constexpr int kTabGroups = 32;
+  static constexpr uint32_t kTotal = kTab;
+  static constexpr uint32_t kTotalTab = kTab + kTabGroups * kBN * 4;
   static_assert(WK == 1 || CW * 16 * 64 * 16 <= 2 * kBuf, "the K-wave reduction fits the buffers");
 };
 
@@ -121,12 +124,21 @@ struct SkinnyArgs {
 // consecutive groups are one aligned 16-byte block: each staging thread loads one block of each
 // per 8 groups (one window of 8 / WK iterations), a window ahead, instead of one 2-byte load per
 // group (a wave-wide 2-byte load of 64 columns touches as many cache lines as a weight load).
-template <int CW, int WK, int L, bool APERM, bool SZB>
+//
+// TAB (with SZB, at most 32 groups per workgroup): the scales and zeros of the workgroup's groups
+// are loaded once, before the loop, into an LDS table, instead of a window of 16-byte blocks per
+// staging thread in registers; the registers this frees carry a deeper weight and activation ring
+// (L = 3). Per-iteration timestamps of the L = 2 kernel showed each iteration waiting about as long
+// for the next group's activations as it computes: the loads' latency under a full GPU is about
+// two iterations.
+template <int CW, int WK, int L, bool APERM, bool SZB, bool TAB = false>
 __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs args) {
   using LDS = SkLds<CW, WK>;
+  static_assert(!TAB || SZB, "the table is loaded in 16-byte blocks");
   constexpr int W = 8 / WK;              // iterations per window of 8 groups
-  constexpr int U = L > W ? L : W;       // main-loop unroll: static ring slots and window positions
-  static_assert(U % L == 0 && U % W == 0, "unroll covers whole rings and windows");
+  // main-loop unroll: static ring slots, LDS buffer parities and (without TAB) window positions
+  constexpr int U = TAB ? (L % 2 == 0 ? L : 2 * L) : (L > W ? L : W);
+  static_assert(U % L == 0 && U % 2 == 0 && (TAB || U % W == 0), "unroll covers whole rings and windows");
   constexpr int BN = LDS::kBN, TG = 64 * CW;  // columns per tile; threads per K-wave
   constexpr int AC = 1024 / TG;               // 16-byte activation chunks a thread stages per group
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -213,7 +225,11 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
     }
     // the column record of group WK i + qs of this K-wave (past the range: never read, no update)
     uint32_t sv, zv;
-    if constexpr (SZB) {
+    if constexpr (TAB) {
+      const uint32_t sz = reinterpret_cast<const uint32_t*>(smem + LDS::kTab)[min(WK * i + qs, ng - 1) * BN + u];
+      sv = sz & 0xFFFFu;
+      zv = sz >> 16;
+    } else if constexpr (SZB) {
       if (p == 0) {
         if (i > 0) {  // uniform: the window's blocks, loaded a window ago
           sb_cur = sb_nxt;
@@ -287,19 +303,39 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
   // then refills that slot with iteration i + L, waits for iteration i + 1's activations (issued
   // L - 1 iterations earlier; only the later iterations' loads stay in flight), stages them into
   // the other buffer, and crosses the one barrier of the iteration.
-  if constexpr (SZB) issue_blocks(0, sb_cur, zb_cur);
+  if constexpr (TAB) {  // the two staging threads of a column take alternate blocks of 8 groups
+    uint32_t* tab = reinterpret_cast<uint32_t*>(smem + LDS::kTab);
+    for (int blk = qs; blk < (ng + 7) / 8; blk += WK) {
+      const uint4 sb = ldg16(C.sc, szc_off + uint32_t(g0 + 8 * blk) * 2u);
+      const uint4 zb = ldg16(C.zr, szc_off + uint32_t(g0 + 8 * blk) * 2u);
+      const uint32_t sw[4] = {sb.x, sb.y, sb.z, sb.w}, zw[4] = {zb.x, zb.y, zb.z, zb.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        tab[(8 * blk + e) * BN + u] =
+            ((sw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) | (((zw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
+    }
+  } else if constexpr (SZB) {
+    issue_blocks(0, sb_cur, zb_cur);
+  }
 #pragma unroll
   for (int s = 0; s < L; ++s) issue(s, s);
+  if constexpr (TAB) __syncthreads();  // the table (the other staging thread's blocks)
   stage(0, 0, 0, 0);
   __syncthreads();
   // step s of an unrolled round: iteration i = round start + s (i % U == s)
+  // With the three-deep ring (TAB) the two K-waves run the iteration's halves in opposite orders:
+  // K-wave 0 computes and then stages iteration i + 1, K-wave 1 stages first (its registers for
+  // i + 1 were requested two iterations ago) and then computes. A SIMD holds one wave of each
+  // K-wave, so its matrix core works while the other wave stages instead of both waves
+  // contending for it and then both staging.
+  const bool stage_first = TAB && wk == 1;  // uniform per wave
   auto step = [&](int i, int s) {
+    if (stage_first && i + 1 < iters) stage((s + 1) % L, (s + 1) & 1, i + 1, (s + 1) % W);
     compute(s % L, s & 1, i);
     issue(s % L, i + L);
-    if (i + 1 < iters) stage((s + 1) % L, (s + 1) & 1, i + 1, (s + 1) % W);
+    if (!stage_first && i + 1 < iters) stage((s + 1) % L, (s + 1) & 1, i + 1, (s + 1) % W);
     __syncthreads();
   };
-  static_assert(L % 2 == 0, "the ring depth keeps buffer and slot parities aligned");
   const int nfull = iters - iters % U;
   for (int i = 0; i < nfull; i += U) {
 #pragma unroll
@@ -366,17 +402,19 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
 
 constexpr int kCW = 4;
 constexpr int kWK = 2;
-constexpr int kL = 2;
+constexpr int kL = 2;     // ring depth with a window of scale blocks in registers
+constexpr int kLTab = 3;  // ring depth with the scale table in LDS
 constexpr int kTileN = 64 * kCW;
 
-template <bool APERM, bool SZB>
+template <bool APERM, bool SZB, bool TAB>
 hipError_t launch_args(const SkinnyArgs& a, int grid, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&skinny_kernel<kCW, kWK, kL, APERM, SZB>);
-  const size_t lds = SkLds<kCW, kWK>::kTotal;
+  constexpr int L = TAB ? kLTab : kL;
+  const void* fn = reinterpret_cast<const void*>(&skinny_kernel<kCW, kWK, L, APERM, SZB, TAB>);
+  const size_t lds = TAB ? SkLds<kCW, kWK>::kTotalTab : SkLds<kCW, kWK>::kTotal;
   if (lds > 64 * 1024) {
     if (hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds))) return e;
   }
-  hipLaunchKernelGGL((skinny_kernel<kCW, kWK, kL, APERM, SZB>), dim3(grid), dim3(64 * kCW * kWK), lds, st, a);
+  hipLaunchKernelGGL((skinny_kernel<kCW, kWK, L, APERM, SZB, TAB>), dim3(grid), dim3(64 * kCW * kWK), lds, st, a);
   return hipGetLastError();
 }
 
@@ -413,8 +451,10 @@ bool skinny_takes(int M, int D, int N) {
 hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t st, std::vector<ReduceCall>* defer) {
   std::vector<ReduceCall> own;
   std::vector<ReduceCall>& reduces = defer ? *defer : own;
-  for (int variant = 0; variant < 4; ++variant) {
-    const int x_perm = variant & 1, szb = variant >> 1;
+  // variants: x's word order; 16-byte scale blocks (G and every split start a multiple of 8 groups)
+  // or not; with blocks, the scale table when every workgroup has at most 32 groups
+  for (int variant = 0; variant < 6; ++variant) {
+    const int x_perm = variant & 1, szb = variant >= 2, tab = variant >= 4;
     int i = 0;
     while (i < n) {
       SkinnyArgs a;
@@ -432,6 +472,7 @@ hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t s
         }
         // 16-byte blocks of 8 groups' scales: G and every split start a multiple of 8
         if (int((j.D / PARO_GROUP) % 8 == 0 && p.gps % 8 == 0) != szb) continue;
+        if (szb && int(p.gps <= SkLds<kCW, kWK>::kTabGroups) != tab) continue;
         SkinnyCall& c = a.c[a.n++];
         c.x = j.x;
         c.qw = j.qweight;
@@ -451,8 +492,11 @@ hipError_t launch_skinny(const SkinnyJob* jobs, int n, int ydtype, hipStream_t s
         if (p.splits > 1) reduces.push_back(reduce_call(static_cast<const float*>(j.ws), j.y, j.M, j.N, j.N, p.splits));
       }
       if (a.n == 0) continue;
-      hipError_t e = szb ? (x_perm ? launch_args<true, true>(a, grid, st) : launch_args<false, true>(a, grid, st))
-                         : (x_perm ? launch_args<true, false>(a, grid, st) : launch_args<false, false>(a, grid, st));
+      hipError_t e = tab   ? (x_perm ? launch_args<true, true, true>(a, grid, st) : launch_args<false, true, true>(a, grid, st))
+                     : szb ? (x_perm ? launch_args<true, true, false>(a, grid, st)
+                                     : launch_args<false, true, false>(a, grid, st))
+                           : (x_perm ? launch_args<true, false, false>(a, grid, st)
+                                     : launch_args<false, false, false>(a, grid, st));
       if (e != hipSuccess) return e;
     }
   }
