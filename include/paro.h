@@ -195,8 +195,9 @@ paro_status paro_w4a16_linear(int M, int D, int N, const void* x, const uint8_t*
  * operand) immediately followed by the INT4 linear of paro_w4a16_linear, with
  * the weights packed by paro_pack_weights for the same transform. With M <= 16,
  * D <= 4096, K <= 8 and (ceil(M / 4) - 1) * (N * D / 2 + N * D / 32) <= 16 MiB
- * (the transform runs per 4-row unit and every unit reads all the weights) the
- * transform runs inside the decode kernel (one launch, no workspace);
+ * (the transform runs per 4-row unit and every unit reads all the weights), or
+ * with M = 1, 4096 < D <= 9216 and K <= 8, the transform runs inside the
+ * decode kernel (one launch, no workspace);
  * otherwise a transform kernel writes x' into ws, which must
  * then hold at least paro_workspace_bytes(M, D, N) bytes (else
  * PARO_EWORKSPACE; the rest of it serves the linear as above), and the linear

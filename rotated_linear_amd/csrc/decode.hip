@@ -53,9 +53,18 @@ constexpr int kThreads = kDecodeThreads;
 constexpr int kWaves = kThreads / 64;
 // transform stages whose records are loaded ahead: 4 (measured on the batched attention step:
 // 13.2 us per step with all 8 stages' records requested up front, 12.6 with 4, 13.1 with 2; every
-// workgroup asks for them at once, and the first stages' records then wait behind the later ones)
-__host__ __device__ constexpr int ring_stages(int) { return 4; }
+// workgroup asks for them at once, and the first stages' records then wait behind the later ones);
+// 2 for rows wider than 4096 channels, whose records take more registers per stage
+__host__ __device__ constexpr int ring_stages(int ppt) { return ppt > 4 ? 2 : 4; }
 constexpr int kFusedPairIt = 4;  // channel pairs per thread in the transform prologue (D / 2 <= 2048)
+// Rows wider than 4096 channels run the transform inside as one-row units (their rows and 1/s take
+// 8 D bytes of LDS), up to 9 channel pairs per thread.
+constexpr int kFusedWidePairIt = 9;
+// The prologue's registers for a launch whose transforms take PPT pairs per thread: XP channel
+// pairs of XR rows each, and XV float4 of 1/s.
+__host__ __device__ constexpr int fused_xp(int ppt) { return ppt > kFusedPairIt ? ppt : kFusedPairIt; }
+__host__ __device__ constexpr int fused_xr(int ppt) { return ppt > kFusedPairIt ? 1 : 4; }
+__host__ __device__ constexpr int fused_xv(int ppt) { return (fused_xp(ppt) + 1) / 2; }
 constexpr int kPlainX = 8;      // x loads per thread staging a plain unit (rows * D / 8 <= 4096)
 constexpr int kCUs = 256;       // MI355X compute units: one workgroup each
 constexpr size_t kLdsLimit = 144 * 1024;
@@ -112,17 +121,18 @@ __device__ inline h8 decode_order(h8 a) { return __builtin_shufflevector(a, a, 0
 // unit_finish: the K stages, then x' = rows * (1/s) as float16 chunks in the decode order. Both
 // LDS passes move whole R-row channel vectors with consecutive lanes on consecutive channels,
 // so they stay (nearly) free of bank conflicts.
-template <int R>
-__device__ inline void unit_fill(float* rot, float* isl, const uint32_t (&xp)[kFusedPairIt][4],
-                                 const float4 (&iv)[2], int D, int tid) {
+template <int R, int XP, int XR, int XV>
+__device__ inline void unit_fill(float* rot, float* isl, const uint32_t (&xp)[XP][XR], const float4 (&iv)[XV], int D,
+                                 int tid) {
+  static_assert(R <= XR, "the unit's rows are in registers");
   using V = typename RowVec<R>::T;
   V* rv = reinterpret_cast<V*>(rot);
   const int P = D / 2;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < XV; ++u)
     if (tid + u * kThreads < D / 4) reinterpret_cast<float4*>(isl)[tid + u * kThreads] = iv[u];
 #pragma unroll
-  for (int u = 0; u < kFusedPairIt; ++u) {
+  for (int u = 0; u < XP; ++u) {
     const int cp = tid + u * kThreads;  // channels 2 cp (low half) and 2 cp + 1
     if (cp < P) {
       float f0[R], f1[R];
@@ -222,8 +232,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   // ---- loads the weights must not delay (issued first, so waiting for them never waits for
   // a weight): x, 1/s and the transform records, or the plain x
   StageRing<kThreads, (PPT > 0 ? PPT : 1), PD, false, true> ring;  // PPT = ceil(D/2 / 512)
-  uint32_t xp[kFusedPairIt][4];  // x channel pair tid + u * 512 of row r (rows past the unit repeat)
-  float4 iv[2];
+  constexpr int XP = fused_xp(PPT), XR = fused_xr(PPT), XV = fused_xv(PPT);
+  uint32_t xp[XP][XR];  // x channel pair tid + u * 512 of row r (rows past the unit repeat)
+  float4 iv[XV];
   uint4 pv[kPlainX];
   if constexpr (fused) {
     {
@@ -231,9 +242,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
       // while the stage records behind them are needed one stage at a time
       const gptr<const uint32_t> x32 = (gptr<const uint32_t>)ix;
 #pragma unroll
-      for (int u = 0; u < kFusedPairIt; ++u)
+      for (int u = 0; u < XP; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < XR; ++r) {
           // uniform guards: only the pairs and rows the unit has
           xp[u][r] = 0u;
           if (u * kThreads < D / 2 && r < rows) {
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
           }
         }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < XV; ++u) {
         int e = tid + u * kThreads;
         e = e < D / 4 ? e : D / 4 - 1;
         iv[u] = __builtin_bit_cast(float4, ld16(inv_s + size_t(e) * 4));
@@ -270,7 +281,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   // weights issued next land during the stages.
   float* const rot = reinterpret_cast<float*>(smem + L.rot);
   float* const isl = reinterpret_cast<float*>(smem + L.isv);
-  if constexpr (fused) {
+  if constexpr (fused && XR == 1) {
+    unit_fill<1>(rot, isl, xp, iv, D, tid);  // wide rows: one-row units
+  } else if constexpr (fused) {
     const int R = rows_class(rows);
     if (R == 1)
       unit_fill<1>(rot, isl, xp, iv, D, tid);
@@ -320,7 +333,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs args)
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- stage the A operand
-  if constexpr (fused) {
+  if constexpr (fused && XR == 1) {
+    unit_finish<1>(ring, rot, isl, xs, rows, D, K, tid, recs);
+  } else if constexpr (fused) {
     const int R = rows_class(rows);
     if (R == 1)
       unit_finish<1>(ring, rot, isl, xs, rows, D, K, tid, recs);
@@ -490,6 +505,9 @@ hipError_t go(const Plan& p, hipStream_t st) {
 template <int WPT, int GW>
 hipError_t go_ppt(const Plan& p, hipStream_t st) {
   constexpr int maxp = GW == 0 ? 0 : (GW * WPT + 7) / 8;
+  // rows wider than 4096 channels (one-row units): more than 32 groups, so the A operand is read
+  // from LDS (GW = 0) by 8 waves per tile
+  constexpr bool wide = GW == 0 && WPT == 8;
   switch (p.ppt) {
     case 0:
       return go<0, GW, WPT>(p, st);
@@ -504,6 +522,21 @@ hipError_t go_ppt(const Plan& p, hipStream_t st) {
       break;
     case 4:
       if constexpr (maxp >= 4) return go<4, GW, WPT>(p, st);
+      break;
+    case 5:
+      if constexpr (wide) return go<5, GW, WPT>(p, st);
+      break;
+    case 6:
+      if constexpr (wide) return go<6, GW, WPT>(p, st);
+      break;
+    case 7:
+      if constexpr (wide) return go<7, GW, WPT>(p, st);
+      break;
+    case 8:
+      if constexpr (wide) return go<8, GW, WPT>(p, st);
+      break;
+    case 9:
+      if constexpr (wide) return go<9, GW, WPT>(p, st);
       break;
     default:
       break;
@@ -592,8 +625,11 @@ bool decode_takes(int K, int M, int D, int N) {
   // 24-bit row products and 32-bit byte offsets into the packed weights
   if (N >= (1 << 24) || size_t(N) * size_t(D / 2) >= (size_t(1) << 31)) return false;
   if (K < 0) return true;
+  if (K > kUnrolledStages) return false;
+  // wider rows: single-row calls only (one unit, one pass over the weights)
+  if (D > kDecodeFusedMaxD) return M == 1 && D <= kDecodeFusedWideMaxD;
   const size_t weight_bytes = size_t(N) * size_t(D / 2) + size_t(N) * size_t(D / PARO_GROUP) * 4;
-  return D <= kDecodeFusedMaxD && K <= kUnrolledStages && size_t((M + 3) / 4 - 1) * weight_bytes <= kDecodeFusedMaxExtraBytes;
+  return size_t((M + 3) / 4 - 1) * weight_bytes <= kDecodeFusedMaxExtraBytes;
 }
 
 hipError_t launch_decode(int D, int ydtype, const DecodeCall* calls, int count, hipStream_t st) {

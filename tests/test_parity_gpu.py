@@ -292,6 +292,27 @@ def test_inside_and_separate_transform_agree():
     assert mx <= C.MAX_ABS and rel <= C.REL_L2, (mx, rel)
 
 
+@pytest.mark.parametrize("D,N,K", [(4224, 300, 8), (5120, 2000, 0), (8960, 1536, 8), (9216, 77, 3)])
+def test_wide_transform_inside_matches_separate(D, N, K):
+    """Rows wider than 4096 channels: a single-row call runs its transform inside the decode
+    kernel (one-row units, up to 9 channel pairs per thread per stage), a two-row call as its own
+    launch before the linear. Both round x' once to float16 and sum in the same order, so the
+    first row agrees bit for bit; the single-row call also meets the oracle bar."""
+    L = W.custom_linear(47, 2, D, N, K)
+    C.log(f"wide transform inside vs separate launch, D={D} N={N} K={K}")
+    rot = _rot(L)
+    qw, sc, z = rl.paro_pack_weights(rot, C.dev(L.W, torch))
+    xd = C.dev(L.x, torch)
+    for dt in (torch.float16, torch.float32):
+        a = C.host(rl.paro_rotated_linear(rot, xd[:1].contiguous(), qw, sc, z, out_dtype=dt))
+        b = C.host(rl.paro_rotated_linear(rot, xd, qw, sc, z, out_dtype=dt))
+        assert np.array_equal(a.view(np.uint8), b[:1].view(np.uint8)), dt
+    deq = O.dequantize(*C.host_weights((qw, sc, z)))
+    ref = O.f16_rne(O.transform_activations(L.x[:1], L.pairs, L.theta, L.scale)).astype(np.float64) @ deq.T
+    mx, rel = C.linear_metrics(a, ref)
+    assert mx <= C.MAX_ABS and rel <= C.REL_L2, (mx, rel)
+
+
 def test_split_reduction_and_fallback():
     """M = 64: with a workspace the reduction over D is split and the float32 partial sums are
     added in split order; without one the call does not split. Both match the oracle, the
@@ -382,8 +403,9 @@ def _single(rot, xd, w, dt):
     # 40 decode-shaped calls of one D: more units than one decode launch carries (several launches),
     # rotated and plain mixed, M from 1 to 16
     [(200 + i, (1, 2, 4, 16, 3)[i % 5], 512, 24 + 8 * (i % 7), 8 if i % 6 else None) for i in range(40)],
-    # decode-shaped calls whose transform runs outside the decode kernel (D > 4096, K > 8):
-    # batched transforms, then one decode launch per D over the transformed rows
+    # decode-shaped calls whose transform runs outside the decode kernel (D > 4096 with more than
+    # one row, K > 8): batched transforms, then one decode launch per D over the transformed rows;
+    # the single-row calls of D = 4224 run it inside (one-row units)
     [(300 + i, (1, 3, 16, 5)[i % 4], 4224, 40 + 16 * i, 8) for i in range(6)]
     + [(310 + i, (2, 16)[i % 2], 512, 48, 12) for i in range(4)] + [(320, 4, 4224, 64, None)],
     # GEMM-shaped calls of up to 256 rows with different tilings, rotated and plain: grouped
