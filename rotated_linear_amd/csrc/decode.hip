@@ -57,9 +57,9 @@ constexpr int kWaves = kThreads / 64;
 // 2 for rows wider than 4096 channels, whose records take more registers per stage
 __host__ __device__ constexpr int ring_stages(int ppt) { return ppt > 4 ? 2 : 4; }
 constexpr int kFusedPairIt = 4;  // channel pairs per thread in the transform prologue (D / 2 <= 2048)
-// Rows wider than 4096 channels run the transform inside as one-row units (their rows and 1/s take
-// 8 D bytes of LDS), up to 9 channel pairs per thread.
-constexpr int kFusedWidePairIt = 9;
+// Single-row calls wider than kDecodeFusedMaxD channels run the transform inside as one-row units
+// (the row and 1/s take 8 D bytes of LDS) up to this width: 9 channel pairs per thread per stage.
+constexpr int kDecodeFusedWideMaxD = 9216;
 // The prologue's registers for a launch whose transforms take PPT pairs per thread: XP channel
 // pairs of XR rows each, and XV float4 of 1/s.
 __host__ __device__ constexpr int fused_xp(int ppt) { return ppt > kFusedPairIt ? ppt : kFusedPairIt; }

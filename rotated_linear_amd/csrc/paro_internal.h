@@ -83,11 +83,8 @@ bool schedule_stage(int D, std::vector<StagePair>& pairs);
 // ---- decode-shaped linears (decode.hip) ----
 // Largest M the decode kernel takes; above it the tiled MFMA GEMM runs.
 constexpr int kDecodeMaxM = 16;
-// Largest D for which the transform runs inside the decode kernel (units of up to 4 rows), and
-// beyond it, for single-row calls (one-row units: the row and 1/s take 8 D bytes of LDS, and a
-// thread up to 9 channel pairs per stage).
+// Largest D for which the transform runs inside the decode kernel.
 constexpr int kDecodeFusedMaxD = 4096;
-constexpr int kDecodeFusedWideMaxD = 9216;
 // With the transform inside, a call runs as units of up to 4 rows and every unit streams all
 // of the call's weights. Past this many extra weight bytes (units - 1 times the packed weights,
 // scales and zeros) the transform runs as its own launch and the linear as 16-row units: on
