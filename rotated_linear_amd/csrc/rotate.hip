@@ -2,8 +2,8 @@
 // then division by the channel scales ("ParoQuant: pairwise rotations that
 // survive deployment", section "A rotation small enough to execute").
 //
-// One workgroup of NT threads (512; 1024 for a single row wider than 6144 channels,
-// which would otherwise leave each thread 9-14 pairs per stage) holds R rows in LDS as float32, interleaved by
+// One workgroup of NT threads (512; 1024 for rows wider than 6144 channels, whose
+// blocks fill the LDS of a CU on their own) holds R rows in LDS as float32, interleaved by
 // channel (lds[c * R + r]: one R-wide vector per channel, so a stage moves a pair
 // of channels for all R rows with two vector reads and two vector writes), runs
 // the K stages (rotation_core.h) and writes fp16(rows * (1/s)). Workgroups are
@@ -235,18 +235,25 @@ hipError_t launch_ppt(const RotJobs& J, int grid, hipStream_t st) {
   if (P <= 1536) return launch_exact<512, R, 3, (R == 4 ? 2 : 4), PERM>(J, grid, st);
   if (P <= 2048) return launch_exact<512, R, 4, (R == 1 ? 4 : 2), PERM>(J, grid, st);
   if (P <= 3072) return launch_exact<512, R, 6, (R == 2 ? 1 : 2), PERM>(J, grid, st);
-  if constexpr (R == 1) {  // one wide row per workgroup (few rows): 1024 threads, half the pairs each
+  // Wider rows: a workgroup's rows fill most of the LDS, so one workgroup runs per CU; 1024
+  // threads (half the pairs each) give that CU twice the waves to overlap the stages' LDS
+  // round trips. Measured on MI355X, K = 8: 64 x 14336 18.2 -> 14.3 us (one row per workgroup),
+  // 2048 x 8960 50.8 -> 45.0 us (4 rows), 4096 x 14336 164 -> 154 us and 1024 x 14336
+  // 46.6 -> 40.8 us (2 rows). With 2 or 4 rows the record ring is one stage deep: at 1024
+  // threads a deeper ring spills, which was slower still (2048 x 8960: 58.7 us).
+  // Past 14336 channels 8 pairs per thread would spill at 1024 threads: 512 threads, 16 pairs each.
+  if constexpr (R == 1) {
     if (P <= 4608) return launch_exact<1024, R, 5, 2, PERM>(J, grid, st);
     if (P <= 6144) return launch_exact<1024, R, 6, 2, PERM>(J, grid, st);
     if (P <= 7168) return launch_exact<1024, R, 7, 2, PERM>(J, grid, st);
-  }
-  if (P <= 4608) return launch_exact<512, R, 9, 2, PERM>(J, grid, st);
-  if constexpr (R <= 2) {  // wider rows (D > 9216) never take 4 rows per workgroup
-    // two stages of records in flight where the registers allow it (no spills): one stage
-    // leaves every stage waiting for its records' round trip
-    if (P <= 6144) return launch_exact<512, R, 12, 2, PERM, (R == 1 ? 2 : 1)>(J, grid, st);
-    if (P <= 7168) return launch_exact<512, R, 14, 2, PERM, (R == 1 ? 2 : 1)>(J, grid, st);
     return launch_exact<512, R, 16, 1, PERM>(J, grid, st);
+  } else if constexpr (R == 2) {
+    if (P <= 4608) return launch_exact<1024, R, 5, 2, PERM>(J, grid, st);
+    if (P <= 6144) return launch_exact<1024, R, 6, 1, PERM>(J, grid, st);
+    if (P <= 7168) return launch_exact<1024, R, 7, 1, PERM>(J, grid, st);
+    return launch_exact<512, R, 16, 1, PERM>(J, grid, st);
+  } else {  // 4-row blocks only up to 9216 channels
+    if (P <= 4608) return launch_exact<1024, R, 5, 1, PERM>(J, grid, st);
   }
   return hipErrorInvalidValue;
 }
