@@ -109,7 +109,8 @@ size_t paro_rotation_bytes(int K, int D);
  * paro_rotation_prepare.
  *
  * Descriptor layout (each section starts at a multiple of 256 bytes, in order):
- *   struct { uint32 i | (j << 16); float cos; float sin; } rec[K][D/2]   (12 bytes each)
+ *   struct { uint32 4i | (4j << 16); float cos; float sin; } rec[K][D/2]   (12 bytes each;
+ *          4i and 4j are the channels' byte offsets in a float32 row, < 65536 as D <= 16384)
  *   float  inv_s[D]        float32(1 / s)
  *   float  s[D]
  * Within a stage the pairs are stored in a library-chosen order, and a pair

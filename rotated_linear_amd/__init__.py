@@ -217,7 +217,7 @@ def descriptor_sections(buf: np.ndarray, K: int, D: int):
     o_s = o_inv + up(D * 4)
     rec = buf[:P * 12].view(np.uint32).reshape(K, D // 2, 3)
     raw = rec[:, :, 0]
-    pairs = np.stack([raw & 0xFFFF, raw >> 16], axis=-1).astype(np.int64)
+    pairs = np.stack([(raw & 0xFFFF) >> 2, raw >> 18], axis=-1).astype(np.int64)  # fields 4 i, 4 j
     cs = rec[:, :, 1:3].copy().view(np.float32)
     return pairs, cs, buf[o_inv:o_inv + D * 4].view(np.float32), buf[o_s:o_s + D * 4].view(np.float32)
 

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(int N, int D, i
   for (int k = 0; k < K; ++k) {
     for (int p = tid; p < P; p += kPackThreads) {
       const PairRec r = recs[size_t(k) * P + p];
-      const int i = int(r.ij & 0xFFFFu), j = int(r.ij >> 16);
+      const int i = int((r.ij & 0xFFFFu) >> 2), j = int(r.ij >> 18);  // the fields are 4 i and 4 j
       const double c = r.c, sn = r.s;
       const double bi = brow[i], bj = brow[j];
       brow[i] = c * bi + sn * bj;

@@ -190,7 +190,7 @@ paro_status paro_rotation_encode(int K, int D, const int32_t* pairs_host, const 
     if (!schedule_stage(D, stage)) return PARO_EPAIRS;
     for (int p = 0; p < P; ++p) {
       PairRec& r = rec[size_t(k) * P + p];
-      r.ij = uint32_t(stage[p].i) | (uint32_t(stage[p].j) << 16);
+      r.ij = (uint32_t(stage[p].i) * 4u) | ((uint32_t(stage[p].j) * 4u) << 16);  // byte offsets in a float32 row
       r.c = stage[p].c;
       r.s = stage[p].s;
     }

@@ -32,7 +32,8 @@ __host__ __device__ inline T qw_group_stride(T n, T N) {
 }
 
 // Device descriptor of a prepared transform. Three sections, each 256-byte aligned:
-//   rec    PairRec [K][D/2]  {i | (j << 16), cos, sin} (12 bytes: one 3-dword load per pair)
+//   rec    PairRec [K][D/2]  {4 i | (4 j << 16), cos, sin} (12 bytes: one 3-dword load per pair;
+//          the channels' byte offsets in one float32 row, D <= 16384)
 //   inv_s  float   [D]       1/s rounded once to float32 (activation side)
 //   s      float   [D]       s (weight side)
 struct PairRec {

@@ -9,7 +9,9 @@
 // orders each stage so a wave's gathers spread over the LDS banks.
 //
 // Per row: x_i <- fma(c, x_i, s x_j), x_j <- fma(c, x_j, -(s x_i)) in float32.
-// Each pair is one 12-byte record {i | j << 16, cos, sin}: one 3-dword load.
+// Each pair is one 12-byte record {4 i | 4 j << 16, cos, sin}: one 3-dword load. The two 16-bit
+// fields are the channels' byte offsets in one float32 row (D <= 16384); R interleaved rows put
+// channel c at byte R * 4 c, so a one-row block uses a field as its LDS address as it stands.
 // The records of PD stages are kept in flight in a register ring: loading
 // stage k + PD is issued right after stage k. Loads are branch-free (indices
 // clamped into range) and the stage sequence is straight-line code for K <= 8,
@@ -66,7 +68,7 @@ __device__ inline typename RowVec<R>::T givens_fma(float c, typename RowVec<R>::
     return __builtin_fmaf(c, a, t);
   } else {
     using V = typename RowVec<R>::T;
-    return __builtin_elementwise_fma(V{} + c, a, t);
+    return __builtin_elementwise_fma(static_cast<V>(c), a, t);  // c splat (no 0 + c add)
   }
 }
 
@@ -113,14 +115,29 @@ struct StageRing {
   __device__ inline void apply(typename RowVec<R>::T* rows, int P, int tid) const {
     using V = typename RowVec<R>::T;
     constexpr int B = (16 / R) < PPT ? (16 / R) : PPT;
+    // the channel vector of a record's first (hi = false) or second field (4 c): a one-row block
+    // uses the field as its LDS byte offset, an R-row block indexes its vectors by c = field / 4
+    // (kept a value of its own, so one shift-add forms the address instead of shift, mask, add)
+    auto at = [rows](uint32_t w, bool hi) -> V* {
+      if constexpr (R == 1) {
+        return reinterpret_cast<V*>(reinterpret_cast<char*>(rows) + (hi ? w >> 16 : w & 0xFFFFu));
+      } else {
+        uint32_t c = hi ? w >> 18 : (w & 0xFFFFu) >> 2;
+        asm("" : "+v"(c));
+        return rows + c;
+      }
+    };
 #pragma unroll
     for (int q0 = 0; q0 < PPT; q0 += B) {
       V vi[B], vj[B];
+      V *pi[B], *pj[B];  // each pair's two addresses, formed once for its gather and its update
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         if (q0 + b < PPT) {
-          vi[b] = rows[ij[slot][q0 + b] & 0xFFFFu];
-          vj[b] = rows[ij[slot][q0 + b] >> 16];
+          pi[b] = at(ij[slot][q0 + b], false);
+          pj[b] = at(ij[slot][q0 + b], true);
+          vi[b] = *pi[b];
+          vj[b] = *pj[b];
         }
       }
 #pragma unroll
@@ -128,8 +145,8 @@ struct StageRing {
         const int q = q0 + b;
         if (q < PPT && (EXACT || (TIGHT && q + 1 < PPT) || tid + q * NT < P)) {
           const float c = cs[slot][q], s = sn[slot][q];
-          rows[ij[slot][q] & 0xFFFFu] = givens_fma<R>(c, vi[b], s * vj[b]);
-          rows[ij[slot][q] >> 16] = givens_fma<R>(c, vj[b], -(s * vi[b]));
+          *pi[b] = givens_fma<R>(c, vi[b], s * vj[b]);
+          *pj[b] = givens_fma<R>(c, vj[b], -(s * vi[b]));
         }
       }
     }
