@@ -283,6 +283,9 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
       mk[tn] = k.w;
     }
     const unsigned char* A = base + uint32_t(wk) * kGroupBytes + uint32_t(r16) * (kLdaH * 2) + uint32_t(q) * 64u;
+    // the wave issuing its MFMAs goes first on its SIMD (the other wave there is staging): the
+    // 8B-class decode step's linears 62.6 -> 61.0 us
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       h8 a[4];
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
         for (int r = 0; r < 4; ++r) acc[r][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[r], bf, acc[r][tn], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- main loop. Iteration i computes from LDS buffer i % 2 with weights from ring slot i % L,
