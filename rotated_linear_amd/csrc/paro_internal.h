@@ -131,7 +131,8 @@ struct DecodeArgs {
 };
 
 // Whether the decode kernel takes a call of this shape: K < 0 for a plain linear, else the
-// transform's stage count (the transform then runs inside the kernel: K <= 8, D <= 4096).
+// transform's stage count (the transform then runs inside the kernel: K <= 8 and D <= 4096, or a
+// single row of up to 9216 channels).
 bool decode_takes(int K, int M, int D, int N);
 // Launch the decode kernel over calls that share D (several launches when the units exceed
 // one launch's table).
