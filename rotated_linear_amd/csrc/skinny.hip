@@ -127,10 +127,10 @@ struct SkinnyArgs {
 //
 // TAB (with SZB, at most 32 groups per workgroup): the scales and zeros of the workgroup's groups
 // are loaded once, before the loop, into an LDS table, instead of a window of 16-byte blocks per
-// staging thread in registers; the registers this frees carry a deeper weight and activation ring
-// (L = 3). Per-iteration timestamps of the L = 2 kernel showed each iteration waiting about as long
-// for the next group's activations as it computes: the loads' latency under a full GPU is about
-// two iterations.
+// staging thread in registers, and the two K-waves are staggered (below). Per-iteration
+// timestamps of the kernel without the table showed each iteration waiting about as long for the
+// next group's activations as it computes. A three-deep ring measured no faster than two with the
+// table, and slower once the wave issuing its MFMAs took issue priority.
 template <int CW, int WK, int L, bool APERM, bool SZB, bool TAB = false>
 __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs args) {
   using LDS = SkLds<CW, WK>;
@@ -327,9 +327,9 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
   stage(0, 0, 0, 0);
   __syncthreads();
   // step s of an unrolled round: iteration i = round start + s (i % U == s)
-  // With the three-deep ring (TAB) the two K-waves run the iteration's halves in opposite orders:
+  // With the scale table (TAB) the two K-waves run the iteration's halves in opposite orders:
   // K-wave 0 computes and then stages iteration i + 1, K-wave 1 stages first (its registers for
-  // i + 1 were requested two iterations ago) and then computes. A SIMD holds one wave of each
+  // i + 1 were requested an iteration ago) and then computes. A SIMD holds one wave of each
   // K-wave, so its matrix core works while the other wave stages instead of both waves
   // contending for it and then both staging.
   const bool stage_first = TAB && wk == 1;  // uniform per wave
@@ -406,13 +406,12 @@ __global__ __launch_bounds__(64 * CW * WK) void skinny_kernel(const SkinnyArgs a
 
 constexpr int kCW = 4;
 constexpr int kWK = 2;
-constexpr int kL = 2;     // ring depth with a window of scale blocks in registers
-constexpr int kLTab = 3;  // ring depth with the scale table in LDS
+constexpr int kL = 2;  // ring depth (iterations of loads in flight)
 constexpr int kTileN = 64 * kCW;
 
 template <bool APERM, bool SZB, bool TAB>
 hipError_t launch_args(const SkinnyArgs& a, int grid, hipStream_t st) {
-  constexpr int L = TAB ? kLTab : kL;
+  constexpr int L = kL;
   const void* fn = reinterpret_cast<const void*>(&skinny_kernel<kCW, kWK, L, APERM, SZB, TAB>);
   const size_t lds = TAB ? SkLds<kCW, kWK>::kTotalTab : SkLds<kCW, kWK>::kTotal;
   if (lds > 64 * 1024) {
