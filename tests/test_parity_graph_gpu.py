@@ -32,9 +32,10 @@ def _calls(specs):
 
 @pytest.mark.parametrize("specs", [
     # decode-shaped: two D (the second D's transforms on the side stream), 17..64-row calls in one
-    # skinny launch with a split reduction, a plain call, an M <= 16 call on the decode kernel
+    # skinny launch with a split reduction, a plain call, an M <= 16 call on the decode kernel and
+    # a single-row call of 8960 channels with its transform inside the decode kernel
     [(700, 64, 512, 256, 8), (701, 64, 512, 96, 8), (702, 40, 1024, 128, 8), (703, 64, 4224, 64, 8),
-     (704, 33, 512, 64, None), (705, 8, 512, 64, 8)],
+     (704, 33, 512, 64, None), (705, 8, 512, 64, 8), (706, 1, 8960, 96, 8)],
     # prefill-shaped: three long rotated calls (transforms ahead on the side stream, ready events),
     # a long plain call and a short rotated call
     [(710, 300, 512, 96, 8), (711, 257, 1024, 64, 2), (712, 400, 512, 128, 12), (713, 300, 512, 64, None),
