@@ -247,20 +247,31 @@ size_t paro_linear_batch_workspace_bytes(int count, const paro_linear_args* call
 /*
  * paro_linear_batch -- `count` independent linears of the kind above (a decode
  * step's projections, say), each computing bit for bit what its single call
- * computes. The decode-shaped calls
- * (M <= 16) that share D run as one launch of the decode kernel, their
- * transforms inside it where the single call would; for the others, the
- * transforms of the calls with M <= 256 that share D run as one launch (or as
- * few as the GPU holds at once); the decode-shaped ones among them (M <= 16,
- * with D or K past what the decode kernel runs inside) then run their linears
- * as one decode launch per D; the GEMM-shaped linears of up to 256 rows that
- * share a tiling run as one launch (and their split reductions as one more),
- * longer calls one at a time (a rotated one's transform right before its
- * linear); each call uses its own
- * consecutive slice of ws (ws_bytes >= paro_linear_batch_workspace_bytes). The calls may run concurrently, so no
- * call's y may overlap any buffer of another call (PARO_EINVAL); every call is
- * checked as its single call would be before anything is enqueued. The
- * `calls` array is read during the call only (host memory).
+ * computes, in as few launches as their shapes allow:
+ *   - decode-shaped calls (M <= 16) that share D: one decode-kernel launch,
+ *     their transforms inside it where the single call runs them there;
+ *   - the other rotated calls of up to 256 rows: their transforms as one launch
+ *     per D (or as few as the GPU holds at once); the decode-shaped ones among
+ *     them (D or K past what the decode kernel runs inside) then run their
+ *     linears as one decode launch per D;
+ *   - calls of 17..64 rows: one skinny-kernel launch per kernel variant (x word
+ *     order, scale layout), their split reductions one launch at the end; other
+ *     calls of up to 256 rows that share a GEMM tiling: one grouped launch, its
+ *     split reductions one more;
+ *   - longer calls one at a time, a rotated one's transform right before its
+ *     linear or, with two or more long rotated calls, all their transforms
+ *     ahead on the library's second stream, each linear waiting for its own.
+ * When the rotated calls have several D, the transforms of every D but the one
+ * with the most packed weight bytes run on the library's second stream,
+ * concurrently with the rest. The second stream joins `stream` through events:
+ * both are created per device on the first batch that needs them, outside any
+ * stream capture (a batch whose first use falls inside a capture runs on
+ * `stream` alone, with the same kernels and results). Each call uses its own
+ * consecutive slice of ws (ws_bytes >= paro_linear_batch_workspace_bytes). The
+ * calls may run concurrently, so no call's y may overlap any buffer of another
+ * call (PARO_EINVAL); every call is checked as its single call would be before
+ * anything is enqueued. The `calls` array is read during the call only (host
+ * memory).
  */
 paro_status paro_linear_batch(int count, const paro_linear_args* calls, int ydtype, void* ws,
                               size_t ws_bytes, void* stream);
