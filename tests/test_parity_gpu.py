@@ -313,6 +313,19 @@ def test_wide_transform_inside_matches_separate(D, N, K):
     assert mx <= C.MAX_ABS and rel <= C.REL_L2, (mx, rel)
 
 
+def _wide_sweep(n):
+    rng = np.random.default_rng(2024)
+    return [(int(128 * rng.integers(33, 73)), int(rng.integers(1, 700)), int(rng.integers(0, 9))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("D,N,K", _wide_sweep(8))
+def test_wide_transform_inside_sweep(D, N, K):
+    """Seeded random single-row shapes past 4096 channels (D up to 9216, ragged N, K = 0..8): the
+    transform inside the decode kernel agrees bit for bit with the two-launch path of a two-row
+    call, and meets the oracle bar."""
+    test_wide_transform_inside_matches_separate(D, N, K)
+
+
 def test_split_reduction_and_fallback():
     """M = 64: with a workspace the reduction over D is split and the float32 partial sums are
     added in split order; without one the call does not split. Both match the oracle, the
