@@ -44,12 +44,15 @@ def _check(L, rot, w, dt):
 def test_noalloc_matches_workspace_call_twice(dt):
     """Two calls in a row through the scratch, the second smaller (the scratch then holds the first
     call's larger leftovers), each bit-identical to the workspace call and within the oracle bar;
-    then a decode-shaped call (transform inside the decode kernel: no scratch)."""
+    then decode-shaped calls (transform inside the decode kernel: no scratch), one of them a single
+    row of 8960 channels."""
     big = _case(1301, 300, 4096, 1024, 8)  # transform kernel + GEMM with split partials in the scratch
     small = _case(1302, 40, 1024, 200, 8)
     dec = _case(1303, 4, 1536, 512, 8)
+    wide = _case(1305, 1, 8960, 256, 8)
     for name, (L, rot, w) in (("M=300 D=4096 N=1024", big), ("M=40 D=1024 N=200", small),
-                              ("M=4 D=1536 N=512", dec), ("M=300 D=4096 N=1024 again", big)):
+                              ("M=4 D=1536 N=512", dec), ("M=1 D=8960 N=256", wide),
+                              ("M=300 D=4096 N=1024 again", big)):
         C.log(f"noalloc {name} {dt}")
         _check(L, rot, w, dt)
 
